@@ -1,0 +1,146 @@
+/*
+ * fa.h -- C ABI of libfa.so: exact attention forward for AMD MI355X (gfx950).
+ *
+ * Two operations, both exact (no approximation of the softmax):
+ *
+ *   fa_fwd     prefill / self-attention forward over a whole sequence, computed
+ *              tile by tile with an online softmax so the n x n score matrix
+ *              never exists in device memory; key tiles wholly outside the
+ *              causal or sliding-window band are never visited.
+ *   fa_decode  one new query token per sequence attending to its whole paged
+ *              KV cache, split along the cache (flash decoding) and merged by
+ *              log-sum-exp weights.
+ *
+ * Sources (web pages on IO-aware exact attention):
+ *   - charles2530 blog "算子与编译器：FlashAttention 与长上下文": §1 (the
+ *     formula softmax(Q Kᵀ/√d) V), §2 (tiling + online softmax, no score
+ *     matrix in HBM), §4 and §6 (decode reads a long KV history for a short
+ *     query, so it is parallelised along the history), §5 (paged KV).
+ *   - xxqk.cn article on FlashAttention for sliding-window prefill: §3.1-§3.2
+ *     (tiles and the running max / running sum / rescaled accumulator), §4
+ *     (bidirectional band |i-j| <= w; causal range [i-w, i]), §5.1-§5.5 (skip
+ *     key blocks outside the band, mask the partly covered ones before the
+ *     softmax, skipping an all -inf block is exact), §7.1 (the library call
+ *     takes causal and a (left, right) window).
+ *   - "FlashAttention 深度解析：大模型长序列的算力解放" (ruiowl.com), §二 (tiles of
+ *     64-128 tokens staged in on-chip memory), §三 (the result equals standard
+ *     attention).
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *     library never allocates, frees, retains or synchronises; work is
+ *     enqueued on `stream` (a hipStream_t; NULL means the default stream) and
+ *     the call returns at once.  Device-side faults surface at the caller's
+ *     next synchronisation.
+ *   - Tensors are dense and row-major (C order) with the shapes stated below.
+ *   - Return value: FA_OK (0) or a negative fa_status.  Arguments are checked
+ *     on the host before anything is launched; on error nothing is enqueued.
+ *     No function throws across the ABI.
+ *   - Grouped-query attention: query head h uses key/value head
+ *     h / (H / Hkv); H must be a multiple of Hkv.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,        /* a required pointer is NULL                      */
+  FA_ERR_SHAPE = -2,       /* sizes are out of range or inconsistent          */
+  FA_ERR_UNSUPPORTED = -3, /* valid request this build does not implement     */
+  FA_ERR_WORKSPACE = -4,   /* decode workspace missing or too small           */
+  FA_ERR_LAUNCH = -5       /* the HIP runtime rejected a kernel launch        */
+} fa_status;
+
+typedef enum {
+  FA_BF16 = 0, /* bfloat16 storage, fp32 accumulation                  */
+  FA_F32 = 1   /* float32 storage and arithmetic throughout             */
+} fa_dtype;
+
+/*
+ * fa_fwd -- attention forward over whole sequences.
+ *
+ *   q    [B, H,   n, d]  (dtype)
+ *   k, v [B, Hkv, n, d]  (dtype)
+ *   o    [B, H,   n, d]  (dtype, written)
+ *   lse  [B, H,   n]     float32, written: natural-log log-sum-exp of each
+ *                        score row over its visible keys, scale included,
+ *                        lse_i = ln sum_{j visible} exp(scale * q_i . k_j)
+ *
+ * For each row i the visible keys j are (window < 0 means no window):
+ *   causal = 0, window < 0 : all 0 <= j < n
+ *   causal = 1, window < 0 : j <= i
+ *   causal = 0, window >= 0: |i - j| <= window   (bidirectional band)
+ *   causal = 1, window >= 0: i - window <= j <= i
+ * o_i = sum_{j visible} softmax_j(scale * q_i . k_j) v_j.  Every row sees at
+ * least key i, so no row is empty.
+ *
+ * Limits: B, H, Hkv, n >= 1; H % Hkv == 0; d in {64, 128};
+ * B*H*n*d < 2^31 elements per tensor; scale finite.
+ * dtype FA_BF16: MFMA path; FA_F32: float32 path.
+ * Errors: FA_ERR_NULL (q, k, v, o or lse NULL), FA_ERR_SHAPE,
+ * FA_ERR_UNSUPPORTED (d not 64/128 or unknown dtype), FA_ERR_LAUNCH.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int Hkv, int n, int d, int causal, int window,
+           float scale, int dtype, void* stream);
+
+/*
+ * fa_decode_workspace_bytes -- device workspace fa_decode needs for these
+ * sizes (partial outputs and log-sum-exps of every split).  Depends only on
+ * the arguments; 0 if they are out of range.
+ */
+size_t fa_decode_workspace_bytes(int B, int H, int max_seqlen, int d);
+
+/*
+ * fa_decode -- one query token per sequence over a paged KV cache (bf16).
+ *
+ *   q          [B, H, d]                          bf16
+ *   kcache     [num_pages, Hkv, page_size, d]     bf16
+ *   vcache     [num_pages, Hkv, page_size, d]     bf16
+ *   page_table [B, max_pages] int32: physical page of logical page p of
+ *              sequence b; token t of sequence b is slot t % page_size of
+ *              page page_table[b, t / page_size]
+ *   seqlens    [B] int32: cached tokens of each sequence, the new token's own
+ *              key/value already appended; 1 <= seqlens[b] <= max_seqlen and
+ *              ceil(seqlens[b] / page_size) <= max_pages
+ *   o          [B, H, d] bf16, written;  lse [B, H] float32, written
+ *   workspace  device memory of at least
+ *              fa_decode_workspace_bytes(B, H, max_seqlen, d) bytes; its
+ *              contents on entry do not matter and are overwritten.
+ *
+ * The query attends to every cached token of its sequence (no mask).
+ * Device-side guards: a length outside [1, max_seqlen] is clamped into
+ * [0, min(max_seqlen, max_pages*page_size)] and a length of 0 gives o = 0 and
+ * lse = -inf; a page id outside [0, num_pages) is never dereferenced (its
+ * tokens are left out).  Both only keep memory accesses in bounds: the
+ * result for such input is not attention over the intended cache.
+ *
+ * Limits: B, H, Hkv >= 1; H % Hkv == 0; H / Hkv <= 16; d == 128;
+ * page_size == 16; num_pages >= 1; max_pages >= 1; max_seqlen >= 1.
+ * Errors: FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE,
+ * FA_ERR_LAUNCH.
+ */
+int fa_decode(const void* q, const void* kcache, const void* vcache,
+              const int32_t* page_table, const int32_t* seqlens, void* o,
+              float* lse, int B, int H, int Hkv, int d, int num_pages,
+              int page_size, int max_pages, int max_seqlen, float scale,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char* fa_strerror(int status);
+
+/* ABI version of this library: (major << 16) | minor. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

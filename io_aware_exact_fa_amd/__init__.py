@@ -1,0 +1,13 @@
+"""FlashAttention forward (prefill + paged flash-decoding) for MI355X / gfx950.
+
+The compute path is the HIP library ``libfa.so`` built from ``csrc/``; this
+package is a thin ctypes binding over its C ABI (see ``include/fa.h``).
+The library is loaded lazily on first use and loading fails loudly if it has
+not been built.
+"""
+
+from .binding import (  # noqa: F401
+    FA_BF16, FA_F32, FaError, lib, lib_path,
+    fa_fwd, fa_decode, fa_decode_workspace_bytes, fa_strerror, fa_version,
+    flash_attn_fwd, flash_decode,
+)

@@ -1,0 +1,176 @@
+"""ctypes binding over libfa.so (declared in include/fa.h).
+
+Argument marshalling only: tensors become device pointers, the current torch
+stream becomes the hipStream_t, and a negative status becomes ``FaError``.
+Every step of the computation runs in the library's HIP kernels.  Loading
+fails loudly when the library has not been built; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+FA_BF16 = 0
+FA_F32 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class FaError(RuntimeError):
+    """A libfa call returned a negative status."""
+
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {fa_strerror(status)} (status {status})")
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libfa.so")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfa.so once; raise if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build the HIP library first "
+            "(python -c 'import __graft_entry__ as g; g.build()')")
+    L = ctypes.CDLL(path)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                         f32, i32, vp]
+    L.fa_fwd.restype = i32
+    L.fa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    L.fa_decode_workspace_bytes.restype = sz
+    L.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                            i32, i32, i32, f32, vp, sz, vp]
+    L.fa_decode.restype = i32
+    L.fa_strerror.argtypes = [i32]
+    L.fa_strerror.restype = ctypes.c_char_p
+    L.fa_version.argtypes = []
+    L.fa_version.restype = i32
+    _LIB = L
+    return L
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def fa_strerror(status: int) -> str:
+    return lib().fa_strerror(int(status)).decode()
+
+
+def fa_version() -> int:
+    return int(lib().fa_version())
+
+
+def fa_fwd(q, k, v, o, lse, B, H, Hkv, n, d, causal, window, scale, dtype,
+           stream=None) -> None:
+    """Raw C-ABI call; tensors or integer device addresses."""
+    st = lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B),
+                      int(H), int(Hkv), int(n), int(d), int(causal), int(window),
+                      float(scale), int(dtype), _stream(stream))
+    if st != 0:
+        raise FaError(st, "fa_fwd")
+
+
+def fa_decode_workspace_bytes(B, H, max_seqlen, d) -> int:
+    return int(lib().fa_decode_workspace_bytes(int(B), int(H), int(max_seqlen), int(d)))
+
+
+def fa_decode(q, kcache, vcache, page_table, seqlens, o, lse, B, H, Hkv, d,
+              num_pages, page_size, max_pages, max_seqlen, scale, workspace,
+              workspace_bytes, stream=None) -> None:
+    """Raw C-ABI call; tensors or integer device addresses."""
+    st = lib().fa_decode(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(page_table),
+                         _ptr(seqlens), _ptr(o), _ptr(lse), int(B), int(H),
+                         int(Hkv), int(d), int(num_pages), int(page_size),
+                         int(max_pages), int(max_seqlen), float(scale),
+                         _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if st != 0:
+        raise FaError(st, "fa_decode")
+
+
+# ---------------------------------------------------------------------------
+# Convenience wrappers: allocate outputs with torch, then call the ABI.
+# ---------------------------------------------------------------------------
+
+def _check_contig(*ts):
+    for t in ts:
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous (row-major)")
+
+
+def flash_attn_fwd(q, k, v, causal: bool = False, window: int = -1,
+                   scale: float | None = None, out=None, lse=None, stream=None):
+    """q [B,H,n,d], k/v [B,Hkv,n,d] (bf16 or fp32 CUDA tensors) -> (o, lse)."""
+    import torch
+    _check_contig(q, k, v)
+    B, H, n, d = q.shape
+    Hkv = k.shape[1]
+    if q.dtype == torch.bfloat16:
+        dt = FA_BF16
+    elif q.dtype == torch.float32:
+        dt = FA_F32
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if not (k.dtype == v.dtype == q.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    if tuple(k.shape) != (B, Hkv, n, d) or tuple(v.shape) != (B, Hkv, n, d):
+        raise ValueError("k and v must be [B, Hkv, n, d]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, n), dtype=torch.float32, device=q.device)
+    fa_fwd(q, k, v, out, lse, B, H, Hkv, n, d, int(bool(causal)), int(window),
+           scale, dt, stream)
+    return out, lse
+
+
+def flash_decode(q, kcache, vcache, page_table, seqlens, max_seqlen: int,
+                 scale: float | None = None, workspace=None, out=None, lse=None,
+                 stream=None):
+    """q [B,H,d] bf16; caches [P,Hkv,ps,d] bf16; table [B,maxp] / seqlens [B] int32."""
+    import torch
+    _check_contig(q, kcache, vcache, page_table, seqlens)
+    B, H, d = q.shape
+    P, Hkv, ps, d2 = kcache.shape
+    if d2 != d or tuple(vcache.shape) != tuple(kcache.shape):
+        raise ValueError("cache shapes disagree with q")
+    if page_table.dtype != torch.int32 or seqlens.dtype != torch.int32:
+        raise ValueError("page_table and seqlens must be int32")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nbytes = fa_decode_workspace_bytes(B, H, max_seqlen, d)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    fa_decode(q, kcache, vcache, page_table, seqlens, out, lse, B, H, Hkv, d, P,
+              ps, page_table.shape[1], max_seqlen, scale, workspace,
+              workspace.numel() * workspace.element_size(), stream)
+    return out, lse

@@ -1,0 +1,152 @@
+"""Seeded synthetic inputs shared by the HIP path, its tests and the oracle.
+
+This module draws random numbers, rounds them to the storage type and builds
+paged-cache bookkeeping.  It holds none of the attention arithmetic: no
+scores, no softmax, no reductions over keys.
+
+Recipe (fixed so every consumer sees bit-identical inputs):
+  * generator: numpy ``default_rng(seed)`` (PCG64); draws are float32
+    standard normals, ``Generator.standard_normal(dtype=float32)``;
+  * prefill: Q, then K, then V are drawn in that order, each in [B, heads, n, d]
+    C order; an optional ``draw_scale`` multiplies each float32 draw before
+    rounding (0.5 is exact in binary floating point);
+  * bf16 storage: round-to-nearest-even of the float32 draw to bfloat16;
+    the returned float32 arrays hold exactly the rounded values;
+  * decode: from ``default_rng(seed)``: the sequence lengths (discrete uniform
+    on [min_len, max_len], inclusive), then q [B, H, d], then a random
+    permutation of the P physical pages, P = sum_b ceil(L_b / page_size).
+    Sequence b owns logical pages 0..ceil(L_b/ps)-1, mapped in order onto its
+    consecutive slice of that permutation.  Its K and V values come from the
+    generators ``default_rng([seed, 1, b])`` and ``default_rng([seed, 2, b])``
+    as [pages_b, Hkv, page_size, d] draws in logical page order, so one
+    sequence can be regenerated without the others.  Slots past L_b in the last
+    page hold draws too (never visible).  Unused page-table entries are -1.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "bf16_round",
+    "bf16_bits_to_f32",
+    "prefill_inputs",
+    "decode_lengths_and_table",
+    "decode_sequence_kv",
+    "decode_inputs",
+]
+
+
+def bf16_round(x: np.ndarray):
+    """Round float32 values to bfloat16, ties to even.
+
+    Returns (values as float32 holding the rounded numbers, raw uint16 bits).
+    Inputs are finite standard-normal draws; NaN handling is not needed.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    bits = ((u + bias) >> np.uint32(16)).astype(np.uint16)
+    return bf16_bits_to_f32(bits), bits
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32 values."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32)
+            << np.uint32(16)).view(np.float32)
+
+
+def _draw(rng, shape, draw_scale: float) -> np.ndarray:
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if draw_scale != 1.0:
+        x *= np.float32(draw_scale)
+    return x
+
+
+def prefill_inputs(B: int, H: int, Hkv: int, n: int, d: int, seed: int,
+                   dtype: str = "bf16", draw_scale: float = 1.0) -> dict:
+    """Q [B,H,n,d], K and V [B,Hkv,n,d] drawn from ``default_rng(seed)``.
+
+    dtype "bf16": values are rounded to bfloat16 (RNE); the dict holds the
+    float32 views ``q, k, v`` (exact bf16 values) and the raw bits
+    ``q_bits, k_bits, v_bits`` (uint16).  dtype "f32": float32 draws only.
+    """
+    rng = np.random.default_rng(seed)
+    out = {"dtype": dtype, "seed": seed, "shape": (B, H, Hkv, n, d)}
+    for name, heads in (("q", H), ("k", Hkv), ("v", Hkv)):
+        x = _draw(rng, (B, heads, n, d), draw_scale)
+        if dtype == "bf16":
+            vals, bits = bf16_round(x)
+            out[name] = vals
+            out[name + "_bits"] = bits
+        elif dtype == "f32":
+            out[name] = x
+        else:
+            raise ValueError(f"unknown dtype {dtype!r}")
+    return out
+
+
+def decode_lengths_and_table(B: int, H: int, d: int, page_size: int,
+                             min_len: int, max_len: int, seed: int) -> dict:
+    """Sequence lengths, q and the permuted page table (no KV values).
+
+    Returns seqlens [B] int32, q (float32 bf16-exact) and q_bits [B,H,d],
+    page_table [B, max_pages] int32 (-1 where unused), num_pages, max_pages,
+    and first_page [B] (offset of each sequence's slice in the permutation).
+    """
+    rng = np.random.default_rng(seed)
+    seqlens = rng.integers(min_len, max_len + 1, size=B).astype(np.int32)
+    q_vals, q_bits = bf16_round(_draw(rng, (B, H, d), 1.0))
+    pages = (seqlens.astype(np.int64) + page_size - 1) // page_size
+    num_pages = int(pages.sum())
+    perm = rng.permutation(num_pages).astype(np.int32)
+    max_pages = int((max_len + page_size - 1) // page_size)
+    table = np.full((B, max_pages), -1, dtype=np.int32)
+    first = np.zeros(B, dtype=np.int64)
+    off = 0
+    for b in range(B):
+        first[b] = off
+        table[b, :pages[b]] = perm[off:off + pages[b]]
+        off += int(pages[b])
+    return {"seqlens": seqlens, "q": q_vals, "q_bits": q_bits,
+            "page_table": table, "num_pages": num_pages,
+            "max_pages": max_pages, "pages": pages, "first_page": first,
+            "page_size": page_size, "seed": seed}
+
+
+def decode_sequence_kv(seed: int, b: int, pages_b: int, Hkv: int,
+                       page_size: int, d: int):
+    """K and V pages of sequence b in logical order: (k_vals, k_bits, v_vals, v_bits),
+    each [pages_b, Hkv, page_size, d]."""
+    kx = _draw(np.random.default_rng([seed, 1, b]), (pages_b, Hkv, page_size, d), 1.0)
+    vx = _draw(np.random.default_rng([seed, 2, b]), (pages_b, Hkv, page_size, d), 1.0)
+    kv, kb = bf16_round(kx)
+    vv, vb = bf16_round(vx)
+    return kv, kb, vv, vb
+
+
+def decode_inputs(B: int, H: int, Hkv: int, d: int, page_size: int,
+                  min_len: int, max_len: int, seed: int,
+                  with_values: bool = True) -> dict:
+    """Full paged-decode workload: lengths, table, q and the whole KV cache.
+
+    kcache/vcache are [num_pages, Hkv, page_size, d]; ``*_bits`` are the
+    bfloat16 bit patterns, and (when ``with_values``) ``kcache``/``vcache``
+    hold the same numbers as float32.
+    """
+    meta = decode_lengths_and_table(B, H, d, page_size, min_len, max_len, seed)
+    P = meta["num_pages"]
+    k_bits = np.empty((P, Hkv, page_size, d), dtype=np.uint16)
+    v_bits = np.empty((P, Hkv, page_size, d), dtype=np.uint16)
+    for b in range(B):
+        pb = int(meta["pages"][b])
+        _, kb, _, vb = decode_sequence_kv(seed, b, pb, Hkv, page_size, d)
+        phys = meta["page_table"][b, :pb]
+        k_bits[phys] = kb
+        v_bits[phys] = vb
+    meta["kcache_bits"] = k_bits
+    meta["vcache_bits"] = v_bits
+    if with_values:
+        meta["kcache"] = bf16_bits_to_f32(k_bits)
+        meta["vcache"] = bf16_bits_to_f32(v_bits)
+    return meta

@@ -1,0 +1,53 @@
+"""Seeded input generator: bf16 rounding, determinism, page-table structure (CPU)."""
+
+import numpy as np
+import torch
+
+from io_aware_exact_fa_amd.inputs import (bf16_round, decode_inputs,
+                                          decode_lengths_and_table, prefill_inputs)
+
+
+def test_bf16_round_matches_torch_rne():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(100_000, dtype=np.float32),
+                        np.array([0.0, -0.0, 1.0, 1.00390625, 1.01171875, -3.5e-20,
+                                  65504.0, 1e30], dtype=np.float32)])
+    vals, bits = bf16_round(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16)
+    assert np.array_equal(bits, ref.view(torch.int16).numpy().view(np.uint16))
+    assert np.array_equal(vals, ref.to(torch.float32).numpy())
+
+
+def test_prefill_deterministic_and_scaled():
+    a = prefill_inputs(1, 2, 1, 33, 8, seed=4)
+    b = prefill_inputs(1, 2, 1, 33, 8, seed=4)
+    for name in ("q", "k", "v"):
+        assert np.array_equal(a[name + "_bits"], b[name + "_bits"])
+    half = prefill_inputs(1, 2, 1, 33, 8, seed=4, draw_scale=0.5)
+    # x0.5 is exact before rounding, so the rounded values halve exactly
+    assert np.array_equal(half["q"], a["q"] * np.float32(0.5))
+    f = prefill_inputs(1, 1, 1, 5, 4, seed=1, dtype="f32")
+    assert f["q"].dtype == np.float32 and "q_bits" not in f
+
+
+def test_decode_table_is_a_permutation():
+    meta = decode_lengths_and_table(8, 4, 16, 16, 1, 200, seed=5)
+    t = meta["page_table"]
+    used = t[t >= 0]
+    assert sorted(used.tolist()) == list(range(meta["num_pages"]))
+    for b in range(8):
+        pb = int(meta["pages"][b])
+        assert pb == (int(meta["seqlens"][b]) + 15) // 16
+        assert np.all(t[b, :pb] >= 0) and np.all(t[b, pb:] == -1)
+    assert meta["seqlens"].min() >= 1 and meta["seqlens"].max() <= 200
+
+
+def test_decode_cache_places_sequence_pages():
+    meta = decode_inputs(3, 4, 2, 8, 16, 5, 40, seed=6)
+    from io_aware_exact_fa_amd.inputs import decode_sequence_kv
+    for b in range(3):
+        pb = int(meta["pages"][b])
+        kv, kb, vv, vb = decode_sequence_kv(6, b, pb, 2, 16, 8)
+        phys = meta["page_table"][b, :pb]
+        assert np.array_equal(meta["kcache_bits"][phys], kb)
+        assert np.array_equal(meta["vcache"][phys], vv)
