@@ -1,0 +1,252 @@
+"""Benchmark of the attention forward hot path on one MI355X.
+
+One step = one pass over both halves of the path on one batch of synthetic
+input already resident in HBM:
+  * prefill: causal self-attention with grouped-query heads, B=1, H=32,
+    Hkv=8, n=65536, d=128, bf16 (draws x0.5), fp32 lse;
+  * decode: paged flash-decoding, 64 sequences, 32 query / 8 KV heads, d=128,
+    bf16, lengths uniform in [1024, 32768], 16-token pages behind a permuted
+    page table (split kernel + log-sum-exp merge kernel).
+
+Printed: ONE JSON line.  ``value`` is the prefill's useful (in-band) TFLOP/s:
+4*d FLOPs per visible (query, key) pair, divided by the prefill kernel's
+average duration from HIP events on the stream it runs on.  The decode's KV
+GB/s (bytes of K and V that the sequences' lengths make visible, divided by
+split+merge duration) is reported beside it.  ``cpu_baseline`` times the fp64
+oracle on a bounded sample of the same prefill workload on the host cores.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
+
+PREFILL = dict(B=1, H=32, Hkv=8, n=65536, d=128, causal=1, window=-1, seed=4, draw_scale=0.5)
+DECODE = dict(B=64, H=32, Hkv=8, d=128, page_size=16, min_len=1024, max_len=32768, seed=5)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def inband_pairs(n: int, causal: bool, window: int) -> int:
+    """Number of visible (query, key) pairs of one head (closed forms)."""
+    if window >= n - 1 or window < 0:
+        return n * (n + 1) // 2 if causal else n * n
+    w = window
+    if causal:
+        return (w + 1) * n - w * (w + 1) // 2
+    return n * (2 * w + 1) - w * (w + 1)
+
+
+def source_hash(*names) -> str:
+    h = hashlib.sha256()
+    for nm in names:
+        with open(os.path.join(ROOT, "io_aware_exact_fa_amd", "csrc", nm), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key: str, src_hash: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    the summary is missing or was taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, rows_per_head: int, heads: list[int]):
+    """The oracle, as it is, on a bounded sample: `rows_per_head` evenly
+    spread rows of the given heads of the prefill workload."""
+    import numpy as np
+    from oracle import attention_fwd
+    from oracle.attention import default_workers
+
+    n, d = PREFILL["n"], PREFILL["d"]
+    workers = min(16, default_workers())
+    rows = np.linspace(0, n - 1, rows_per_head).astype(np.int64)
+    q = inp["q"][:, heads]
+    group = PREFILL["H"] // PREFILL["Hkv"]
+    kv_heads = sorted(set(h // group for h in heads))
+    # query head h reads key/value head h // group: pass that head along with it
+    k = inp["k"][:, [h // group for h in heads]]
+    v = inp["v"][:, [h // group for h in heads]]
+    t0 = time.perf_counter()
+    attention_fwd(q, k, v, True, -1, 1.0 / math.sqrt(d), rows=rows, workers=workers)
+    dt = time.perf_counter() - t0
+    inband = sum(int(r) + 1 for r in rows) * len(heads)
+    flops = 4 * d * inband
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers,
+            "kind": "oracle",
+            "sample": f"{rows_per_head} evenly spaced query rows x {len(heads)} heads "
+                      f"(KV heads {kv_heads}) of the n=65536 causal prefill, fp64, "
+                      f"{dt:.1f} s wall; in-band FLOPs of those rows only"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-rows", type=int, default=16384,
+                    help="query rows per sampled head for the oracle baseline (>= 1)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): this build "
+              "has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import io_aware_exact_fa_amd as fa
+    from io_aware_exact_fa_amd.inputs import decode_inputs, prefill_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def i32(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(dev)
+
+    P = PREFILL
+    log("generating prefill inputs")
+    pin = prefill_inputs(P["B"], P["H"], P["Hkv"], P["n"], P["d"], seed=P["seed"],
+                         draw_scale=P["draw_scale"])
+    q, k, v = bf(pin["q_bits"]), bf(pin["k_bits"]), bf(pin["v_bits"])
+    o = torch.empty_like(q)
+    lse = torch.empty((P["B"], P["H"], P["n"]), dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(P["d"])
+
+    Dc = DECODE
+    log("generating decode inputs")
+    din = decode_inputs(Dc["B"], Dc["H"], Dc["Hkv"], Dc["d"], Dc["page_size"], Dc["min_len"],
+                        Dc["max_len"], seed=Dc["seed"], with_values=False)
+    dq, dk, dv = bf(din["q_bits"]), bf(din["kcache_bits"]), bf(din["vcache_bits"])
+    dpt, dsl = i32(din["page_table"]), i32(din["seqlens"])
+    do = torch.empty_like(dq)
+    dlse = torch.empty((Dc["B"], Dc["H"]), dtype=torch.float32, device=dev)
+    ws_bytes = fa.fa_decode_workspace_bytes(Dc["B"], Dc["H"], Dc["max_len"], Dc["d"])
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    del din["kcache_bits"], din["vcache_bits"]
+
+    # A plain copy of known size: the reference for HBM counter scaling.
+    cal_src = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+    torch.cuda.synchronize()
+    del cal_src, cal_dst
+
+    stream = torch.cuda.current_stream()
+
+    def prefill():
+        fa.fa_fwd(q, k, v, o, lse, P["B"], P["H"], P["Hkv"], P["n"], P["d"], P["causal"],
+                  P["window"], scale, fa.FA_BF16, stream)
+
+    def decode():
+        fa.fa_decode(dq, dk, dv, dpt, dsl, do, dlse, Dc["B"], Dc["H"], Dc["Hkv"], Dc["d"],
+                     dk.shape[0], Dc["page_size"], dpt.shape[1], Dc["max_len"], scale, ws,
+                     ws_bytes, stream)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        prefill()
+        decode()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record(stream)
+        prefill()
+        e[1].record(stream)
+        decode()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+
+    pairs = inband_pairs(P["n"], bool(P["causal"]), P["window"]) * P["B"] * P["H"]
+    flops = 4 * P["d"] * pairs
+    tflops = flops / (pre_ms * 1e-3) / 1e12
+    kv_bytes = int(np.sum(din["seqlens"].astype(np.int64))) * Dc["Hkv"] * Dc["d"] * 2 * 2
+    gbs = kv_bytes / (dec_ms * 1e-3) / 1e9
+    log(f"prefill {pre_ms:.3f} ms  {tflops:.1f} TFLOP/s   decode {dec_ms:.3f} ms  {gbs:.0f} GB/s")
+
+    pre_hash = source_hash("prefill_bf16.hip", "common.hpp")
+    dec_hash = source_hash("decode.hip", "common.hpp")
+    pre_traffic = measured_traffic("prefill_bf16", pre_hash)
+    dec_traffic = measured_traffic("decode", dec_hash)
+
+    out = {
+        "metric": "prefill attention TFLOP/s (in-band) & % MFMA peak; decode KV GB/s & % HBM peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) draws rounded to bf16)",
+        "config": {
+            "workload": "causal GQA prefill B1 H32/Hkv8 n65536 d128 (draws x0.5) + paged "
+                        "decode B64 H32/Hkv8 d128 L~U[1024,32768] page16",
+            "prefill": {k2: P[k2] for k2 in ("B", "H", "Hkv", "n", "d", "causal", "window")},
+            "decode": {k2: Dc[k2] for k2 in ("B", "H", "Hkv", "d", "page_size", "min_len",
+                                             "max_len")},
+        },
+        "prefill_ms": round(pre_ms, 4),
+        "decode_ms": round(dec_ms, 4),
+        "roofline": {
+            "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": pre_traffic, "kernel": "prefill_bf16_kernel",
+            "algorithmic_flops_per_launch": flops,
+        },
+        "decode": {
+            "value": round(gbs, 1), "unit": "GB/s", "kv_bytes": kv_bytes,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": dec_traffic,
+                         "kernel": "decode_split_kernel + decode_combine_kernel"},
+        },
+    }
+    del q, k, v, o, dq, dk, dv
+    torch.cuda.empty_cache()
+    log("timing the oracle on a bounded sample")
+    out["cpu_baseline"] = cpu_baseline(pin, max(1, args.cpu_rows),
+                                       heads=[0, 5, 10, 15, 16, 21, 26, 31])
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,87 @@
+// C ABI of libfa.so (declared in include/fa.h): argument checks on the host,
+// then dispatch to the gfx950 kernels.  Nothing here allocates, frees or
+// synchronises; every kernel is enqueued on the caller's stream.
+
+#include "../../include/fa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+
+#include "launch.hpp"
+
+namespace {
+
+bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
+
+bool fits_i32(long long x) { return x >= 0 && x < (long long)INT_MAX; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_version(void) { return (1 << 16) | 0; }
+
+const char* fa_strerror(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "sizes out of range or inconsistent";
+    case FA_ERR_UNSUPPORTED: return "request not supported by this build";
+    case FA_ERR_WORKSPACE: return "decode workspace missing or too small";
+    case FA_ERR_LAUNCH: return "kernel launch rejected by the HIP runtime";
+    default: return "unknown status";
+  }
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+           int Hkv, int n, int d, int causal, int window, float scale, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || Hkv < 1 || n < 1 || d < 1) return FA_ERR_SHAPE;
+  if (H % Hkv != 0) return FA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
+  if (!scale_ok(scale)) return FA_ERR_SHAPE;
+  if (!fits_i32((long long)n * d)) return FA_ERR_SHAPE;
+  if (!fits_i32((long long)B * H)) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  // A window of n or more restricts nothing; clamp so index sums cannot overflow.
+  if (window < 0) window = -1;
+  if (window > n) window = n;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == FA_BF16)
+    e = fa::launch_prefill_bf16(q, k, v, o, lse, B, H, Hkv, n, d, causal, window, scale, st);
+  else if (dtype == FA_F32)
+    e = fa::launch_prefill_f32(q, k, v, o, lse, B, H, Hkv, n, d, causal, window, scale, st);
+  else
+    return FA_ERR_UNSUPPORTED;
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+size_t fa_decode_workspace_bytes(int B, int H, int max_seqlen, int d) {
+  if (B < 1 || H < 1 || max_seqlen < 1 || d < 1) return 0;
+  return fa::decode_workspace_bytes(B, H, max_seqlen, d);
+}
+
+int fa_decode(const void* q, const void* kcache, const void* vcache, const int32_t* page_table,
+              const int32_t* seqlens, void* o, float* lse, int B, int H, int Hkv, int d,
+              int num_pages, int page_size, int max_pages, int max_seqlen, float scale,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !kcache || !vcache || !page_table || !seqlens || !o || !lse) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || Hkv < 1 || d < 1 || num_pages < 1 || page_size < 1 || max_pages < 1 ||
+      max_seqlen < 1)
+    return FA_ERR_SHAPE;
+  if (H % Hkv != 0) return FA_ERR_SHAPE;
+  if (!scale_ok(scale)) return FA_ERR_SHAPE;
+  if (!fits_i32((long long)B * H) || !fits_i32((long long)B * max_pages)) return FA_ERR_SHAPE;
+  if (d != 128 || page_size != 16 || H / Hkv > 16) return FA_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < fa::decode_workspace_bytes(B, H, max_seqlen, d))
+    return FA_ERR_WORKSPACE;
+  hipError_t e = fa::launch_decode(q, kcache, vcache, page_table, seqlens, o, lse, B, H, Hkv, d,
+                                   num_pages, max_pages, max_seqlen, scale, workspace,
+                                   static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,31 @@
+// Internal launch entry points behind the C ABI (include/fa.h).
+// Arguments have been validated by the caller; these only build grids and
+// enqueue kernels on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Prefill: q [B,H,n,d], k/v [B,Hkv,n,d], o like q, lse [B,H,n].  window has
+// been clamped to [-1, n].  scale > 0.
+hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* o,
+                               float* lse, int B, int H, int Hkv, int n, int d,
+                               int causal, int window, float scale, hipStream_t stream);
+hipError_t launch_prefill_f32(const void* q, const void* k, const void* v, void* o,
+                              float* lse, int B, int H, int Hkv, int n, int d,
+                              int causal, int window, float scale, hipStream_t stream);
+
+// Decode: tokens per split and the workspace the split partials need.
+int decode_split_pages(int B, int H, int max_seqlen);
+int decode_max_splits(int B, int H, int max_seqlen);
+size_t decode_workspace_bytes(int B, int H, int max_seqlen, int d);
+hipError_t launch_decode(const void* q, const void* kcache, const void* vcache,
+                         const int32_t* page_table, const int32_t* seqlens, void* o,
+                         float* lse, int B, int H, int Hkv, int d, int num_pages,
+                         int max_pages, int max_seqlen, float scale, void* workspace,
+                         hipStream_t stream);
+
+}  // namespace fa

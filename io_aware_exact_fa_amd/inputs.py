@@ -25,6 +25,9 @@ Recipe (fixed so every consumer sees bit-identical inputs):
 
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 __all__ = [
@@ -87,15 +90,25 @@ def prefill_inputs(B: int, H: int, Hkv: int, n: int, d: int, seed: int,
 
 
 def decode_lengths_and_table(B: int, H: int, d: int, page_size: int,
-                             min_len: int, max_len: int, seed: int) -> dict:
+                             min_len: int, max_len: int, seed: int,
+                             seqlens=None) -> dict:
     """Sequence lengths, q and the permuted page table (no KV values).
+
+    ``seqlens`` (optional, each in [min_len, max_len]) replaces the drawn
+    lengths; the length draw is still made so the later draws do not move.
 
     Returns seqlens [B] int32, q (float32 bf16-exact) and q_bits [B,H,d],
     page_table [B, max_pages] int32 (-1 where unused), num_pages, max_pages,
     and first_page [B] (offset of each sequence's slice in the permutation).
     """
     rng = np.random.default_rng(seed)
-    seqlens = rng.integers(min_len, max_len + 1, size=B).astype(np.int32)
+    drawn = rng.integers(min_len, max_len + 1, size=B).astype(np.int32)
+    if seqlens is None:
+        seqlens = drawn
+    else:
+        seqlens = np.asarray(seqlens, dtype=np.int32).reshape(B)
+        if seqlens.min() < min_len or seqlens.max() > max_len:
+            raise ValueError("seqlens outside [min_len, max_len]")
     q_vals, q_bits = bf16_round(_draw(rng, (B, H, d), 1.0))
     pages = (seqlens.astype(np.int64) + page_size - 1) // page_size
     num_pages = int(pages.sum())
@@ -127,23 +140,30 @@ def decode_sequence_kv(seed: int, b: int, pages_b: int, Hkv: int,
 
 def decode_inputs(B: int, H: int, Hkv: int, d: int, page_size: int,
                   min_len: int, max_len: int, seed: int,
-                  with_values: bool = True) -> dict:
+                  with_values: bool = True, seqlens=None) -> dict:
     """Full paged-decode workload: lengths, table, q and the whole KV cache.
 
     kcache/vcache are [num_pages, Hkv, page_size, d]; ``*_bits`` are the
     bfloat16 bit patterns, and (when ``with_values``) ``kcache``/``vcache``
     hold the same numbers as float32.
     """
-    meta = decode_lengths_and_table(B, H, d, page_size, min_len, max_len, seed)
+    meta = decode_lengths_and_table(B, H, d, page_size, min_len, max_len, seed,
+                                    seqlens=seqlens)
     P = meta["num_pages"]
     k_bits = np.empty((P, Hkv, page_size, d), dtype=np.uint16)
     v_bits = np.empty((P, Hkv, page_size, d), dtype=np.uint16)
-    for b in range(B):
+
+    def fill(b):
         pb = int(meta["pages"][b])
         _, kb, _, vb = decode_sequence_kv(seed, b, pb, Hkv, page_size, d)
         phys = meta["page_table"][b, :pb]
         k_bits[phys] = kb
         v_bits[phys] = vb
+
+    # Sequences use independent generators and disjoint pages, so they can be
+    # filled concurrently (numpy releases the GIL while drawing).
+    with ThreadPoolExecutor(max_workers=max(1, min(8, os.cpu_count() or 1))) as ex:
+        list(ex.map(fill, range(B)))
     meta["kcache_bits"] = k_bits
     meta["vcache_bits"] = v_bits
     if with_values:

@@ -1,0 +1,100 @@
+"""C-ABI library: loads, exports every declared symbol, rejects bad arguments
+on the host before any launch (CPU only: no kernel is ever enqueued here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import io_aware_exact_fa_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+FAKE = 256  # a non-NULL address that validation rejects before any use
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.lib_path()):
+        pytest.fail("libfa.so is not built (run __graft_entry__.build())")
+    return fa.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == {"fa_fwd", "fa_decode", "fa_decode_workspace_bytes",
+                          "fa_strerror", "fa_version"}
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_strerror(lib):
+    assert fa.fa_version() >> 16 == 1
+    for st in (0, -1, -2, -3, -4, -5):
+        assert fa.fa_strerror(st) and fa.fa_strerror(st) != "unknown status"
+    assert fa.fa_strerror(-99) == "unknown status"
+
+
+def _fwd(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=2, Hkv=1, n=16, d=128,
+                causal=0, window=-1, scale=0.1, dtype=0)
+    args.update(kw)
+    return fa.lib().fa_fwd(args["q"], args["k"], args["v"], args["o"], args["lse"],
+                           args["B"], args["H"], args["Hkv"], args["n"], args["d"],
+                           args["causal"], args["window"], ctypes.c_float(args["scale"]),
+                           args["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(o=None), -1),
+    (dict(lse=None), -1),
+    (dict(B=0), -2), (dict(H=0), -2), (dict(Hkv=0), -2), (dict(n=0), -2), (dict(d=0), -2),
+    (dict(H=3, Hkv=2), -2), (dict(causal=2), -2), (dict(scale=0.0), -2),
+    (dict(scale=-1.0), -2), (dict(scale=float("inf")), -2), (dict(scale=float("nan")), -2),
+    (dict(n=1 << 25, d=128), -2),
+    (dict(d=96), -3), (dict(d=256), -3), (dict(dtype=7), -3),
+])
+def test_fwd_rejects(lib, kw, status):
+    assert _fwd(**kw) == status
+
+
+def _dec(**kw):
+    args = dict(q=FAKE, kc=FAKE, vc=FAKE, pt=FAKE, sl=FAKE, o=FAKE, lse=FAKE, B=2, H=8,
+                Hkv=2, d=128, P=10, ps=16, maxp=4, maxs=64, scale=0.1, ws=FAKE,
+                wsb=1 << 30)
+    args.update(kw)
+    return fa.lib().fa_decode(args["q"], args["kc"], args["vc"], args["pt"], args["sl"],
+                              args["o"], args["lse"], args["B"], args["H"], args["Hkv"],
+                              args["d"], args["P"], args["ps"], args["maxp"], args["maxs"],
+                              ctypes.c_float(args["scale"]), args["ws"], args["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(kc=None), -1), (dict(vc=None), -1), (dict(pt=None), -1),
+    (dict(sl=None), -1), (dict(o=None), -1), (dict(lse=None), -1),
+    (dict(B=0), -2), (dict(H=0), -2), (dict(Hkv=0), -2), (dict(P=0), -2), (dict(ps=0), -2),
+    (dict(maxp=0), -2), (dict(maxs=0), -2), (dict(H=6, Hkv=4), -2), (dict(scale=0.0), -2),
+    (dict(d=64), -3), (dict(ps=32), -3), (dict(H=34, Hkv=2), -3),
+    (dict(ws=None), -4), (dict(wsb=16), -4),
+])
+def test_decode_rejects(lib, kw, status):
+    assert _dec(**kw) == status
+
+
+def test_workspace_size(lib):
+    assert fa.fa_decode_workspace_bytes(0, 8, 64, 128) == 0
+    small = fa.fa_decode_workspace_bytes(2, 8, 64, 128)
+    big = fa.fa_decode_workspace_bytes(64, 32, 32768, 128)
+    assert 0 < small < big
+    # partial output (d floats) + log-sum-exp per (b, h, split), at least
+    assert big >= 64 * 32 * (32768 // 512) * (128 + 1) * 4
+    ws = fa.fa_decode_workspace_bytes(2, 8, 64, 128)
+    assert _dec(wsb=ws - 1) == -4
