@@ -13,7 +13,9 @@
 //     the matching key/value tile on chip at a time.
 //
 // gfx950 design (prior art above is NVIDIA-shaped; this is not a translation):
-//   * Workgroup = NW waves of 64 lanes; wave w owns 32*NQB query rows.
+//   * Workgroup = NW waves of 64 lanes; wave w owns 32 query rows.  Registers
+//     are kept under 256 per lane so two workgroups share a CU: one's softmax
+//     (vector ALU) overlaps the other's matrix-core work.
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 dims (one ds_read_b128 per
 //     lane from LDS), B = Q^T fragment held in VGPRs for the whole loop.  In the
@@ -22,11 +24,17 @@
 //     one cross-half swap (v_permlane32_swap) -- no LDS round trip.
 //   * The same registers, rounded to bf16, are directly the B operand P^T of
 //     the O^T += V^T P^T MFMA: the MFMA's k index is mapped onto the key order
-//     the accumulator layout produced, and V^T is gathered from LDS to match.
-//   * Softmax runs in the base-2 domain: scale*log2(e) is folded into one FMA
-//     before v_exp_f32.
-//   * K/V tiles are double-buffered in LDS; the next tile's global loads are
-//     in flight while the current tile is computed; one barrier per tile.
+//     the accumulator layout produced.  V stays row-major in LDS and its
+//     transposed fragments come from ds_read_b64_tr_b16 (two per fragment).
+//   * Softmax runs in the base-2 domain with scale*log2(e) folded into one FMA
+//     before v_exp_f32.  A row's reference max moves only when its tile max
+//     exceeds it by more than 2^8 (the same reference divides numerator and
+//     denominator, so the result is unchanged); most tiles skip the
+//     accumulator rescale.
+//   * K/V tiles go HBM -> LDS directly (global_load_lds_dwordx4, no staging
+//     registers), double-buffered: the next tile's loads are in flight during
+//     the current tile; one barrier per tile.  Tiles are dense with an XOR
+//     chunk swizzle instead of padding.
 //   * Grid order: heaviest causal query tiles first; inside each round of B*H
 //     tiles, workgroups that share a key/value head are placed on the same XCD
 //     (dispatch is round-robin over the 8 XCDs), so their K/V reads share L2.
@@ -46,20 +54,44 @@ struct PrefillArgs {
   float scale_log2;  // scale * log2(e)
 };
 
-template <int D, int NW, int NQB, int BC>
-__global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a) {
-  constexpr int BR = NW * 32 * NQB;   // query rows per workgroup
-  constexpr int LS = D + 8;           // LDS row stride in elements (16 B pad)
-  constexpr int NT = NW * 64;
+// LDS tiles are dense (no padding): row r of a tile holds D bf16 values as
+// 16-byte chunks, and logical chunk c of row r sits at physical chunk
+// c ^ swz(r).  The swizzle spreads the 16-byte row reads of the K fragments
+// (8-16 consecutive rows, one chunk each) and the 8-byte transposed reads of
+// the V fragments (4 consecutive rows, 4 chunks each) over distinct banks.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128)
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+  else
+    return row & 7;
+}
+
+// Reference-max update threshold (base-2 exponent units).  The reference max
+// of a row only moves when the tile max exceeds it by more than this, so
+// probabilities stay <= 2^8 and most tiles skip the accumulator rescale.
+constexpr float kRescaleThreshold = 8.0f;
+
+template <int D, int NW, int BC>
+__global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a) {
+  constexpr int BR = NW * 32;         // query rows per workgroup (32 per wave)
+  constexpr int RB = D * 2;           // bytes per tile row
   constexpr int CPR = D / 8;          // 16-byte chunks per row
-  constexpr int CPT = BC * CPR / NT;  // chunks per thread per tensor per tile
+  constexpr int TILE_BYTES = BC * RB;
+  constexpr int IPW = BC * CPR / (64 * NW);  // direct-to-LDS loads per wave per tensor
   constexpr int NKB = BC / 32;        // 32-key MFMA blocks per tile
   constexpr int NDC = D / 16;         // 16-wide head-dim chunks (QK^T contraction)
   constexpr int NDB = D / 32;         // 32-wide head-dim blocks (PV output)
   constexpr int NKC = BC / 16;        // 16-key chunks (PV contraction)
-  static_assert(BC * CPR % NT == 0, "tile must split evenly over threads");
+  static_assert(BC * CPR % (64 * NW) == 0, "tile must split evenly over waves");
 
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2][2][BC * LS];
+  // Double-buffered K and V tiles (BC x D bf16 each).  Four separate objects,
+  // so the compiler can tell the tile being read from the tile being filled
+  // by the in-flight HBM->LDS loads and does not wait for those loads.
+  __shared__ __attribute__((aligned(1024))) char sK0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sV0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sK1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sV1[TILE_BYTES];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
@@ -94,192 +126,211 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs a) {
   const int kt_lo = max(lo_of(q0), 0) / BC;
   const int kt_hi = hi_of(qlast) / BC;
 
-  // ---- this wave's query rows ----
-  const int wq0 = q0 + wave * 32 * NQB;
+  // ---- this wave's 32 query rows; lane owns row wq0 + l32 ----
+  const int wq0 = q0 + wave * 32;
   const bool wave_rows = wq0 < n;
-  const int wr1 = min(wq0 + 32 * NQB, n) - 1;
+  const int wr1 = min(wq0 + 32, n) - 1;
   const int wlo0 = lo_of(wq0), whi0 = hi_of(wq0);
   const int wlo1 = lo_of(wr1), whi1 = hi_of(wr1);
+  const int row = wq0 + l32;
+  const int rlo = lo_of(row), rhi = hi_of(row);
 
-  bf16x8 qf[NQB][NDC];
+  // Q^T fragments (B operand): query row l32, dims 16*dc + 8*hi .. +8.
+  bf16x8 qf[NDC];
 #pragma unroll
-  for (int nq = 0; nq < NQB; ++nq) {
-    const int row = wq0 + nq * 32 + l32;
+  for (int dc = 0; dc < NDC; ++dc)
+    qf[dc] = (row < n) ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)row * D + dc * 16 + hi * 8)
+                       : bf16x8{};
+
+  f32x16 acc[NDB];
 #pragma unroll
-    for (int dc = 0; dc < NDC; ++dc) {
-      if (row < n)
-        qf[nq][dc] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)row * D + dc * 16 + hi * 8);
-      else
-        qf[nq][dc] = bf16x8{};
-    }
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+  float m_ref = kNegInf;  // reference max (base-2 scaled units) of this lane's row
+  float l_run = 0.f;      // this lane's share of the row sum (pair with lane ^ 32)
+
+  // ---- direct HBM -> LDS staging of one K/V tile ----
+  // Wave instruction j writes 64 consecutive 16-byte slots; slot s holds
+  // physical chunk s % CPR of tile row s / CPR.  Rows past the end of the
+  // sequence load row n-1 (finite data; those keys are masked).
+  int st_goff[IPW];
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) {
+    const int s = (wave * IPW + j) * 64 + lane;
+    const int r = s / CPR;
+    const int c = (s % CPR) ^ swz<D>(r);
+    st_goff[j] = r * D + c * 8;  // element offset inside a tile of rows
   }
-
-  f32x16 acc[NQB][NDB];
-  float m_run[NQB], l_run[NQB];
-#pragma unroll
-  for (int nq = 0; nq < NQB; ++nq) {
-    m_run[nq] = kNegInf;
-    l_run[nq] = 0.f;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) acc[nq][db] = f32x16{};
-  }
-
-  // ---- K/V staging: global -> registers -> LDS ----
-  u32x4 stK[CPT], stV[CPT];
-  auto gload = [&](int kt) {
+  auto stage = [&](int kt, char* tk, char* tv) {
     const int k0 = kt * BC;
+    const int last = n - 1 - k0;  // rows beyond this are past the sequence
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * NT;
-      const int r = ch / CPR, cc = ch - (ch / CPR) * CPR;
-      const int key = k0 + r;
-      if (key < n) {
-        stK[c] = *reinterpret_cast<const u32x4*>(Kh + (size_t)key * D + cc * 8);
-        stV[c] = *reinterpret_cast<const u32x4*>(Vh + (size_t)key * D + cc * 8);
-      } else {
-        stK[c] = u32x4{};
-        stV[c] = u32x4{};
-      }
+    for (int j = 0; j < IPW; ++j) {
+      const int r = ((wave * IPW + j) * 64 + lane) / CPR;
+      const int off = r <= last ? st_goff[j] : (last * D + (st_goff[j] - r * D));
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(Kh + (size_t)k0 * D + off),
+          (__attribute__((address_space(3))) void*)(tk + (wave * IPW + j) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(Vh + (size_t)k0 * D + off),
+          (__attribute__((address_space(3))) void*)(tv + (wave * IPW + j) * 1024), 16, 0, 0);
     }
   };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * NT;
-      const int r = ch / CPR, cc = ch - (ch / CPR) * CPR;
-      *reinterpret_cast<u32x4*>(&smem[buf][0][r * LS + cc * 8]) = stK[c];
-      *reinterpret_cast<u32x4*>(&smem[buf][1][r * LS + cc * 8]) = stV[c];
-    }
-  };
+
+  // Per-lane LDS byte offsets of the fragments (tile-relative).
+  // K fragment (kb, dc): row kb*32 + l32, logical chunk 2*dc + hi.
+  // V^T fragment (db, kc, half): 8-byte transposed read; lane supplies row
+  // 16*kc + 8*half + 4*hi + (lane%16)/4 and dims db*32 + 16*((lane/16)%2) + 4*(lane%4).
+  const int krow_sw = swz<D>(l32);
+  const int vrow = 4 * hi + ((lane & 15) >> 2);
+  // swz depends on row bits 0-3: adding 16*kc keeps it, adding 8*half does not.
+  const int vrow_sw[2] = {swz<D>(vrow), swz<D>(vrow + 8)};
+  const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   const float c2 = a.scale_log2;
 
-  gload(kt_lo);
-  sstore(0);
-  __syncthreads();
-
-  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-    const int buf = (kt - kt_lo) & 1;
-    if (kt < kt_hi) gload(kt + 1);
+  // One key tile from LDS (Ks, Vs): S^T = K Q^T, masked online softmax,
+  // O^T += V^T P^T.
+  auto tile = [&](int kt, const char* Ks, const char* Vs) __attribute__((always_inline)) {
     const int k0 = kt * BC, k1 = k0 + BC - 1;
-    // Wave-level classification of this tile against the wave's rows.
     const bool active = wave_rows && !(k1 < wlo0 || k0 > whi1);
     const bool full = (k0 >= wlo1) && (k1 <= whi0);
-    if (active) {
-      const __bf16* Ks = smem[buf][0];
-      const __bf16* Vs = smem[buf][1];
-      // S^T = K Q^T for NKB key blocks x NQB query blocks.
-      f32x16 s[NQB][NKB];
+    if (!active) return;
+    // S^T = K Q^T; the K fragments of the next head-dim chunk are read while
+    // the current chunk's MFMAs run.
+    auto kfrag = [&](int dc, int kb) {
+      const int off = (kb * 32 + l32) * RB + (((2 * dc + hi) ^ krow_sw) << 4);
+      return *reinterpret_cast<const bf16x8*>(Ks + off);
+    };
+    f32x16 s[NKB];
+    bf16x8 kcur[NKB], knext[NKB];
 #pragma unroll
-      for (int nq = 0; nq < NQB; ++nq)
+    for (int kb = 0; kb < NKB; ++kb) {
+      s[kb] = f32x16{};
+      kcur[kb] = kfrag(0, kb);
+    }
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) s[nq][kb] = f32x16{};
+    for (int dc = 0; dc < NDC; ++dc) {
+      if (dc + 1 < NDC) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-        for (int dc = 0; dc < NDC; ++dc) {
-          const bf16x8 kf =
-              *reinterpret_cast<const bf16x8*>(Ks + (kb * 32 + l32) * LS + dc * 16 + hi * 8);
-#pragma unroll
-          for (int nq = 0; nq < NQB; ++nq)
-            s[nq][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[nq][dc], s[nq][kb], 0, 0, 0);
-        }
+        for (int kb = 0; kb < NKB; ++kb) knext[kb] = kfrag(dc + 1, kb);
       }
-      // Online softmax, one query row per lane (pair of lanes l, l^32).
-      bf16x8 pf[NQB][NKC];
 #pragma unroll
-      for (int nq = 0; nq < NQB; ++nq) {
-        if (!full) {
-          const int row = wq0 + nq * 32 + l32;
-          const int rlo = lo_of(row), rhi = hi_of(row);
+      for (int kb = 0; kb < NKB; ++kb)
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur[kb], qf[dc], s[kb], 0, 0, 0);
 #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
+      for (int kb = 0; kb < NKB; ++kb) kcur[kb] = knext[kb];
+    }
+    if (!full) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-              if (key < rlo || key > rhi) s[nq][kb][r] = kNegInf;
-            }
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (key < rlo || key > rhi) s[kb][r] = kNegInf;
         }
-        float mx = kNegInf;
+    }
+    float mx = kNegInf;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmax2(mx, s[nq][kb][r]);
-        mx = max_xor32(mx);
-        const float m_new = fmax2(m_run[nq], mx * c2);
-        // A row with no visible key so far keeps m = -inf; use 0 so that
-        // exp2(-inf - m) stays 0 instead of NaN.
-        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-        const float alpha = exp2_fast(m_run[nq] - m_use);
-        float rs = 0.f;
+      for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[kb][r]);
+    mx = max_xor32(mx) * c2;
+    // Move the reference max only when the row max outgrows it by more than
+    // the threshold (or on the row's first visible key); wave-uniform branch.
+    const bool need = mx > m_ref + kRescaleThreshold;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float alpha = need ? exp2_fast(m_ref - mx) : 1.f;
+      m_ref = need ? mx : m_ref;
+      l_run *= alpha;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+      for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+    }
+    // A row with nothing visible yet keeps m_ref = -inf and sees only -inf
+    // scores here; use 0 so exp2(-inf - m) is 0 rather than NaN.
+    const float m_use = (m_ref == kNegInf) ? 0.f : m_ref;
+    bf16x8 pf[NKC];
+    float rs = 0.f;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float pv = exp2_fast(__builtin_fmaf(s[nq][kb][r], c2, -m_use));
-            rs += pv;
-            pf[nq][kb * 2 + (r >> 3)][r & 7] = (__bf16)pv;
-          }
-        l_run[nq] = alpha * l_run[nq] + rs;
-        m_run[nq] = m_new;
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) acc[nq][db] *= alpha;
+      for (int r = 0; r < 16; ++r) {
+        const float pv = exp2_fast(__builtin_fmaf(s[kb][r], c2, -m_use));
+        rs += pv;
+        pf[kb * 2 + (r >> 3)][r & 7] = (__bf16)pv;
       }
-      // O^T += V^T P^T.  MFMA k index kk = 8*hi + t stands for key
-      // 16*kc + 8*(t/4) + 4*hi + t%4, the order the S^T accumulator holds.
+    l_run += rs;
+    // O^T += V^T P^T.  MFMA k index 8*hi + t stands for key
+    // 16*kc + 8*(t/4) + 4*hi + t%4, the order the S^T accumulator holds.
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
+        bf16x8 vf;
 #pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) {
-          bf16x8 vf;
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const int key = kc * 16 + 8 * (t >> 2) + 4 * hi + (t & 3);
-            vf[t] = Vs[key * LS + db * 32 + l32];
-          }
-#pragma unroll
-          for (int nq = 0; nq < NQB; ++nq)
-            acc[nq][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[nq][kc], acc[nq][db], 0, 0, 0);
+        for (int half = 0; half < 2; ++half) {
+          const int r = 16 * kc + 8 * half + vrow;
+          const int cbyte = (db * 32 + vcol) * 2;
+          const int off = r * RB + ((((cbyte >> 4) ^ vrow_sw[half]) << 4) | (cbyte & 15));
+          typedef short i16x4 __attribute__((ext_vector_type(4)));
+          const i16x4 t4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(
+                  (__attribute__((address_space(3))) char*)(Vs) + off));
+          const bf16x4 b4 = __builtin_bit_cast(bf16x4, t4);
+          vf[4 * half + 0] = b4[0];
+          vf[4 * half + 1] = b4[1];
+          vf[4 * half + 2] = b4[2];
+          vf[4 * half + 3] = b4[3];
         }
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kc], acc[db], 0, 0, 0);
       }
     }
-    if (kt < kt_hi) sstore(buf ^ 1);
+  };
+
+  stage(kt_lo, sK0, sV0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  // Unrolled by two so that each tile's buffer is a fixed LDS object.
+  for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
+    if (kt + 1 <= kt_hi) stage(kt + 1, sK1, sV1);
+    tile(kt, sK0, sV0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kt + 1 > kt_hi) break;
+    if (kt + 2 <= kt_hi) stage(kt + 2, sK0, sV0);
+    tile(kt + 1, sK1, sV1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
   // ---- epilogue: O = acc / l, lse = ln(2) * (m + log2 l) ----
   if (!wave_rows) return;
+  const float lt = sum_xor32(l_run);
+  if (row >= n) return;
+  const float inv = 1.f / lt;
+  __bf16* orow = Oh + (size_t)row * D;
 #pragma unroll
-  for (int nq = 0; nq < NQB; ++nq) {
-    const int row = wq0 + nq * 32 + l32;
-    const float lt = sum_xor32(l_run[nq]);
-    if (row >= n) continue;
-    const float inv = 1.f / lt;
-    __bf16* orow = Oh + (size_t)row * D;
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int g4 = 0; g4 < 4; ++g4) {
+      bf16x4 ov;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        bf16x4 ov;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) ov[j] = (__bf16)(acc[nq][db][4 * g4 + j] * inv);
-        *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * g4 + 4 * hi) = ov;
-      }
-    if (hi == 0) {
-      const float m_use = (m_run[nq] == kNegInf) ? 0.f : m_run[nq];
-      Lh[row] = (m_use + log2_fast(lt)) * kLn2;
+      for (int j = 0; j < 4; ++j) ov[j] = (__bf16)(acc[db][4 * g4 + j] * inv);
+      *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * g4 + 4 * hi) = ov;
     }
+  if (hi == 0) {
+    const float m_use = (m_ref == kNegInf) ? 0.f : m_ref;
+    Lh[row] = (m_use + log2_fast(lt)) * kLn2;
   }
 }
 
 template <int D>
 static hipError_t launch_d(const PrefillArgs& a0, int B, int H, int n, hipStream_t stream) {
-  constexpr int NW = 4, NQB = 1, BC = 64;
-  constexpr int BR = NW * 32 * NQB;
+  constexpr int NW = 4, BC = 64;
+  constexpr int BR = NW * 32;
   PrefillArgs a = a0;
   a.nqb = (n + BR - 1) / BR;
   const long long grid = (long long)a.nqb * B * H;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, NQB, BC>), dim3((unsigned)grid), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, BC>), dim3((unsigned)grid), dim3(NW * 64), 0,
                      stream, a);
   return hipGetLastError();
 }
