@@ -55,6 +55,11 @@ def build(verbose: bool = False) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
+    # Every kernel launched from host code needs its host-side stub defined.
+    nm = subprocess.run(["nm", "-u", tmp], capture_output=True, text=True)
+    missing = [ln.split()[-1] for ln in nm.stdout.splitlines() if "__device_stub__" in ln]
+    if missing:
+        raise RuntimeError(f"undefined kernel stubs in {tmp}: {missing}")
     shutil.move(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

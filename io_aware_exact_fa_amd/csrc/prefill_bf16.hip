@@ -67,6 +67,17 @@ __device__ __forceinline__ int swz(int row) {
     return row & 7;
 }
 
+// 16 bytes per lane from HBM straight into LDS: lane i's bytes land at
+// lds + 16*i; the source is base + off, read as zero when off >= nbytes
+// (buffer descriptor range check).
+__device__ __forceinline__ void buffer_load_lds16(const void* base, int nbytes, unsigned off,
+                                                  void* lds) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           off, 0, 0, 0);
+}
+
 // Reference-max update threshold (base-2 exponent units).  The reference max
 // of a row only moves when the tile max exceeds it by more than this, so
 // probabilities stay <= 2^8 and most tiles skip the accumulator rescale.
@@ -150,29 +161,29 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a)
 
   // ---- direct HBM -> LDS staging of one K/V tile ----
   // Wave instruction j writes 64 consecutive 16-byte slots; slot s holds
-  // physical chunk s % CPR of tile row s / CPR.  Rows past the end of the
-  // sequence load row n-1 (finite data; those keys are masked).
-  int st_goff[IPW];
+  // physical chunk s % CPR of tile row s / CPR.  Loads are buffer loads whose
+  // descriptor (in scalar registers) starts at the tile and ends at the end of
+  // the sequence: each lane's offset is a fixed register, and rows past the
+  // end of the sequence read as zeros by the hardware range check (those keys
+  // are masked and their zero values contribute nothing).
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  unsigned st_off[IPW];
 #pragma unroll
   for (int j = 0; j < IPW; ++j) {
-    const int s = (wave * IPW + j) * 64 + lane;
+    const int s = (wave_u * IPW + j) * 64 + lane;
     const int r = s / CPR;
     const int c = (s % CPR) ^ swz<D>(r);
-    st_goff[j] = r * D + c * 8;  // element offset inside a tile of rows
+    st_off[j] = (unsigned)(r * RB + c * 16);
   }
   auto stage = [&](int kt, char* tk, char* tv) {
     const int k0 = kt * BC;
-    const int last = n - 1 - k0;  // rows beyond this are past the sequence
+    const int bytes = (n - k0) * RB;
+    const __bf16* kb = Kh + (size_t)k0 * D;
+    const __bf16* vb = Vh + (size_t)k0 * D;
 #pragma unroll
     for (int j = 0; j < IPW; ++j) {
-      const int r = ((wave * IPW + j) * 64 + lane) / CPR;
-      const int off = r <= last ? st_goff[j] : (last * D + (st_goff[j] - r * D));
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(Kh + (size_t)k0 * D + off),
-          (__attribute__((address_space(3))) void*)(tk + (wave * IPW + j) * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(Vh + (size_t)k0 * D + off),
-          (__attribute__((address_space(3))) void*)(tv + (wave * IPW + j) * 1024), 16, 0, 0);
+      buffer_load_lds16(kb, bytes, st_off[j], tk + (wave_u * IPW + j) * 1024);
+      buffer_load_lds16(vb, bytes, st_off[j], tv + (wave_u * IPW + j) * 1024);
     }
   };
 
