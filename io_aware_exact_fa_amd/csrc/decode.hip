@@ -56,6 +56,10 @@ __device__ __forceinline__ int decode_len(const DecodeArgs& a, int b) {
   return L > cap ? cap : L;
 }
 
+// Threshold (base-2 exponent units) for moving a query's reference max; see
+// the prefill kernel: the result is unchanged, most pages skip the rescale.
+constexpr float kDecodeRescaleThreshold = 8.0f;
+
 template <int D, int GP>
 __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeArgs a) {
   static_assert(D == 128, "decode kernel is written for head dim 128");
@@ -72,9 +76,17 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
   if (p0 >= npg) return;  // whole workgroup exits together
   const int p1 = min(p0 + a.split_pages, npg);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int G = a.G;
+
+  // This wave's pages are p0 + wave + 4*i, i < cnt; their physical ids are
+  // read once, one per lane, and broadcast with readlane in the loop.
+  const int cnt = p1 - p0 > wave ? (p1 - p0 - wave + kDecodeWaves - 1) / kDecodeWaves : 0;
+  const int32_t* table = a.page_table + (size_t)b * a.max_pages;
+  int my_phys = -1;
+  if (lane < cnt) my_phys = table[p0 + wave + kDecodeWaves * lane];
 
   // Query fragments: B operand (32 dims x 16 query columns) per chunk.
   bf16x8 qf[NC];
@@ -85,7 +97,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
       qf[c] = (col < G) ? *reinterpret_cast<const bf16x8*>(qrow + 32 * c + 8 * grp) : bf16x8{};
   }
 
-  float m_run = kNegInf, l_part = 0.f;
+  float m_ref = kNegInf, l_part = 0.f;
   float acc[GP][8];
 #pragma unroll
   for (int qq = 0; qq < GP; ++qq)
@@ -93,78 +105,89 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
     for (int e = 0; e < 8; ++e) acc[qq][e] = 0.f;
 
   const float c2 = a.scale_log2;
-  const int32_t* table = a.page_table + (size_t)b * a.max_pages;
 
-  for (int p = p0 + wave; p < p1; p += kDecodeWaves) {
-    const int phys = table[p];
-    if (phys < 0 || phys >= a.num_pages) continue;  // never dereference a bad id
+  // Registers of one page: K in the MFMA A-operand layout (token = lane%16,
+  // dims 32c + 8*(lane/16) .. +8) and four V rows (token lane/16 + 4i, dims
+  // 8*(lane%16) .. +8).  A page id outside [0, num_pages) is replaced by page
+  // 0 for the load and all its tokens are masked.
+  struct PageRegs {
+    bf16x8 k[NC];
+    u32x4 v[4];
+  };
+  auto load_page = [&](int i, PageRegs& r) {
+    int phys = __builtin_amdgcn_readlane(my_phys, i);
+    if (phys < 0 || phys >= a.num_pages) phys = 0;
     const size_t base = ((size_t)phys * a.Hkv + g) * kPage * D;
     const __bf16* kp = a.kc + base;
     const __bf16* vp = a.vc + base;
-    bf16x8 kf[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c)
-      kf[c] = *reinterpret_cast<const bf16x8*>(kp + col * D + 32 * c + 8 * grp);
-    u32x4 vr[4];
+      r.k[c] = *reinterpret_cast<const bf16x8*>(kp + col * D + 32 * c + 8 * grp);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      vr[i] = *reinterpret_cast<const u32x4*>(vp + (grp + 4 * i) * D + 8 * col);
+    for (int i4 = 0; i4 < 4; ++i4)
+      r.v[i4] = *reinterpret_cast<const u32x4*>(vp + (grp + 4 * i4) * D + 8 * col);
+  };
+
+  auto process_page = [&](int i, const PageRegs& r) {
+    const int phys = __builtin_amdgcn_readlane(my_phys, i);
+    const bool valid = phys >= 0 && phys < a.num_pages;
+    const int tok0 = (p0 + wave + kDecodeWaves * i) * kPage;
+    // Tokens at or past `lim` are masked (the sequence end, or the whole page
+    // when its id is invalid).
+    const int lim = valid ? L : tok0;
+    const bool tail = tok0 + kPage > lim;
 
     f32x4 sc = f32x4{};
 #pragma unroll
-    for (int c = 0; c < NC; ++c) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[c], qf[c], sc, 0, 0, 0);
-
-    const int tok0 = p * kPage;
-    const bool tail = tok0 + kPage > L;
+    for (int c = 0; c < NC; ++c) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.k[c], qf[c], sc, 0, 0, 0);
     if (tail) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (tok0 + 4 * grp + r >= L) sc[r] = kNegInf;
+      for (int rr = 0; rr < 4; ++rr)
+        if (tok0 + 4 * grp + rr >= lim) sc[rr] = kNegInf;
     }
-    float mx = fmax2(fmax2(sc[0], sc[1]), fmax2(sc[2], sc[3]));
-    mx = max_xor16(mx);
-    mx = max_xor32(mx);
-    const float m_new = fmax2(m_run, mx * c2);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = exp2_fast(m_run - m_use);
-    float pr[4];
-    float ps = 0.f;
+    float mx = __builtin_fmaxf(__builtin_fmaxf(sc[0], sc[1]), __builtin_fmaxf(sc[2], sc[3]));
+    mx = max_xor32(max_xor16(mx)) * c2;
+    const bool need = mx > m_ref + kDecodeRescaleThreshold;
+    const float alpha = need ? exp2_fast(m_ref - mx) : 1.f;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      m_ref = need ? mx : m_ref;
+      l_part *= alpha;
+      float al[GP];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      pr[r] = exp2_fast(__builtin_fmaf(sc[r], c2, -m_use));
-      ps += pr[r];
+      for (int qq = 0; qq < GP; ++qq)
+        al[qq] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), qq));
+#pragma unroll
+      for (int qq = 0; qq < GP; ++qq)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[qq][e] *= al[qq];
     }
-    l_part = alpha * l_part + ps;
-    m_run = m_new;
+    const float m_use = (m_ref == kNegInf) ? 0.f : m_ref;
+    float pr[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      pr[rr] = exp2_fast(__builtin_fmaf(sc[rr], c2, -m_use));
+      l_part += pr[rr];
+    }
 
     // Hand the probabilities to the lanes that hold the matching V rows.
     if (col < GP) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Pl[wave][(4 * grp + r) * GP + col] = pr[r];
+      for (int rr = 0; rr < 4; ++rr) Pl[wave][(4 * grp + rr) * GP + col] = pr[rr];
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    float al[GP];
 #pragma unroll
-    for (int qq = 0; qq < GP; ++qq)
-      al[qq] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), qq));
-#pragma unroll
-    for (int qq = 0; qq < GP; ++qq)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[qq][e] *= al[qq];
-
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = grp + 4 * i;
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int t = grp + 4 * i4;
       float vv[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        vv[2 * e] = bf16lo_to_f32(vr[i][e]);
-        vv[2 * e + 1] = bf16hi_to_f32(vr[i][e]);
+        vv[2 * e] = bf16lo_to_f32(r.v[i4][e]);
+        vv[2 * e + 1] = bf16hi_to_f32(r.v[i4][e]);
       }
-      if (tail && tok0 + t >= L) {
+      if (tail && tok0 + t >= lim) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) vv[e] = 0.f;  // slots past the end may hold anything
       }
@@ -179,6 +202,17 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  // Two register sets: page i+1 is in flight while page i is processed.
+  PageRegs ra, rb;
+  if (cnt > 0) load_page(0, ra);
+  for (int i = 0; i < cnt; i += 2) {
+    if (i + 1 < cnt) load_page(i + 1, rb);
+    process_page(i, ra);
+    if (i + 1 >= cnt) break;
+    if (i + 2 < cnt) load_page(i + 2, ra);
+    process_page(i + 1, rb);
   }
 
   // Sum the four token groups of each column, then merge the waves.
@@ -189,7 +223,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
     for (int e = 0; e < 8; ++e) acc[qq][e] = sum_xor32(sum_xor16(acc[qq][e]));
   if (grp == 0) {
     if (col < GP) {
-      Wm[wave][col] = m_run;
+      Wm[wave][col] = m_ref;
       Wl[wave][col] = l_tot;
     }
 #pragma unroll
@@ -218,27 +252,56 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
   }
 }
 
+// Merge of the splits of one (b, h): one wave; lanes take splits for the
+// max / weight sums and two head dims each for the weighted output sum.
 template <int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
+  static_assert(D == 128, "two head dims per lane");
   const int bh = blockIdx.x;
   const int b = bh / a.H;
-  const int d = threadIdx.x;
+  const int lane = threadIdx.x;
   const int L = decode_len(a, b);
   const int npg = (L + kPage - 1) / kPage;
   const int ns = (npg + a.split_pages - 1) / a.split_pages;
   const float* lse_s = a.ws_lse + (size_t)bh * a.max_splits;
   const float* o_s = a.ws_o + (size_t)bh * a.max_splits * D;
   float M = kNegInf;
-  for (int s = 0; s < ns; ++s) M = fmax2(M, lse_s[s]);
+  for (int s0 = 0; s0 < ns; s0 += 64)
+    if (s0 + lane < ns) M = fmax2(M, lse_s[s0 + lane]);
+  for (int off = 32; off >= 1; off >>= 1) M = fmax2(M, __shfl_xor(M, off));
   const float Mu = (M == kNegInf) ? 0.f : M;
-  float wsum = 0.f, osum = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float wt = exp2_fast(lse_s[s] - Mu);
-    wsum += wt;
-    osum = __builtin_fmaf(wt, o_s[(size_t)s * D + d], osum);
+  float W = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += 64)
+    if (s0 + lane < ns) W += exp2_fast(lse_s[s0 + lane] - Mu);
+  for (int off = 32; off >= 1; off >>= 1) W += __shfl_xor(W, off);
+  float o0 = 0.f, o1 = 0.f;
+  int s = 0;
+  for (; s + 4 <= ns; s += 4) {
+    float w[4];
+    f32x2 x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      w[u] = exp2_fast(lse_s[s + u] - Mu);
+      x[u] = *reinterpret_cast<const f32x2*>(o_s + (size_t)(s + u) * D + 2 * lane);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      o0 = __builtin_fmaf(w[u], x[u][0], o0);
+      o1 = __builtin_fmaf(w[u], x[u][1], o1);
+    }
   }
-  a.o[(size_t)bh * D + d] = (__bf16)(wsum > 0.f ? osum / wsum : 0.f);
-  if (d == 0) a.lse[bh] = wsum > 0.f ? (Mu + log2_fast(wsum)) * kLn2 : kNegInf;
+  for (; s < ns; ++s) {
+    const float w = exp2_fast(lse_s[s] - Mu);
+    const f32x2 x = *reinterpret_cast<const f32x2*>(o_s + (size_t)s * D + 2 * lane);
+    o0 = __builtin_fmaf(w, x[0], o0);
+    o1 = __builtin_fmaf(w, x[1], o1);
+  }
+  const float inv = W > 0.f ? 1.f / W : 0.f;
+  bf16x2 ov;
+  ov[0] = (__bf16)(o0 * inv);
+  ov[1] = (__bf16)(o1 * inv);
+  *reinterpret_cast<bf16x2*>(a.o + (size_t)bh * D + 2 * lane) = ov;
+  if (lane == 0) a.lse[bh] = W > 0.f ? (Mu + log2_fast(W)) * kLn2 : kNegInf;
 }
 
 int decode_split_pages(int B, int H, int max_seqlen) {
@@ -247,6 +310,8 @@ int decode_split_pages(int B, int H, int max_seqlen) {
   (void)max_seqlen;
   return 32;  // 512 tokens per split
 }
+// A wave holds the page ids of its share of a split one per lane.
+static_assert(kDecodeWaves * 64 >= 32, "split pages per wave must fit in 64 lanes");
 
 int decode_max_splits(int B, int H, int max_seqlen) {
   const int sp = decode_split_pages(B, H, max_seqlen);
@@ -299,7 +364,7 @@ hipError_t launch_decode(const void* q, const void* kcache, const void* vcache,
   else return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(B * H), dim3(128), 0, stream, a);
+  hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(B * H), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 
