@@ -11,21 +11,26 @@
 // exp(lse_s - lse), lse = log sum_s exp(lse_s).
 //
 // gfx950 design (HBM bound: every K/V byte is read exactly once):
-//   * One workgroup per (sequence b, key/value head g, split of SPLIT pages);
-//     its 4 waves take the split's pages round-robin.  All G = H/Hkv query
+//   * One workgroup per (sequence b, key/value head g, split of 32 pages);
+//     its 4 waves take the split's pages round-robin, one page (16 tokens) at
+//     a time, with the next page's loads in flight.  All G = H/Hkv query
 //     heads of the group are served from the same K/V bytes.
-//   * Scores: v_mfma_f32_16x16x32_bf16 with A = the page's 16 tokens x 32 dims
-//     loaded straight from HBM into the A-operand layout (16 B per lane), B =
-//     the G query vectors (columns >= G are zero).  In the 16x16 accumulator
-//     lane l owns query column l%16 and 4 tokens; max/sum over the page's 16
-//     tokens are 4 in-lane values plus two lane swaps (permlane16/32).
-//   * Probabilities go through a 1 KB LDS slab per wave; P.V runs on the vector
-//     ALU with each lane owning 8 head dims of one token row, so V rows are
-//     read with coalesced 16 B loads and no transpose is needed.
-//   * Waves merge in LDS at the end; the split writes a normalised fp32
-//     partial output and its base-2 log-sum-exp to the workspace.
-//   * The merge kernel reads the valid splits of each (b, h) and writes bf16
-//     output and the natural-log lse.
+//   * Scores: v_mfma_f32_16x16x32_bf16, A = the page's 16 tokens x 32 dims
+//     loaded straight from HBM into registers in the A-operand layout, B = the
+//     G query vectors (columns >= G are zero).  Lane l owns query column l%16
+//     and tokens 4*(l/16) .. +3, so the max / sum over the page's 16 tokens is
+//     4 in-lane values plus two lane swaps (permlane16/32).
+//   * P.V: v_mfma_f32_16x16x16_bf16 over the page's 16 tokens.  Its B operand
+//     (tokens x query columns) has exactly the score accumulator's layout, so
+//     the bf16-rounded probabilities never leave registers; its A operand
+//     (dims x tokens) comes from the V page, DMA'd HBM -> LDS into a per-wave
+//     buffer and read back transposed with ds_read_b64_tr_b16.  V needs no
+//     registers and the accumulator is 32 registers for any G <= 16.
+//   * The 4 waves merge through LDS at the end (their idle V buffers hold the
+//     partial outputs); the split writes a normalised fp32 partial output and
+//     its base-2 log-sum-exp to the workspace.
+//   * The merge kernel (4 waves per (b, h)) reads the valid splits of each
+//     (b, h) and writes bf16 output and the natural-log lse.
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -60,14 +65,29 @@ __device__ __forceinline__ int decode_len(const DecodeArgs& a, int b) {
 // the prefill kernel: the result is unchanged, most pages skip the rescale.
 constexpr float kDecodeRescaleThreshold = 8.0f;
 
+// Swizzle of the 16-byte chunks of a V page row in LDS (16 rows x 256 B):
+// chunk c of row r sits at c ^ vswz(r), so the transposed reads of one
+// instruction (16 rows x 32 B) spread over all banks in two passes.
+__device__ __forceinline__ int vswz(int r) { return 2 * (r & 7); }
+
+// 16 bytes per lane from HBM straight into LDS (lane i -> lds + 16*i).
+__device__ __forceinline__ void dma16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
 template <int D, int GP>
 __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeArgs a) {
   static_assert(D == 128, "decode kernel is written for head dim 128");
-  constexpr int NC = D / 32;  // 32-dim chunks of the QK contraction
-  __shared__ float Pl[kDecodeWaves][kPage * GP];
-  __shared__ float Wm[kDecodeWaves][GP];
-  __shared__ float Wl[kDecodeWaves][GP];
-  __shared__ float Wacc[kDecodeWaves][GP][D];
+  constexpr int NC = D / 32;   // 32-dim chunks of the QK contraction
+  constexpr int NDB = D / 16;  // 16-dim blocks of the PV output
+  constexpr int PAGE_BYTES = kPage * D * 2;
+  // Per wave: two V page buffers (double-buffered), filled by LDS DMA.
+  __shared__ __attribute__((aligned(1024))) char sV0[kDecodeWaves][PAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sV1[kDecodeWaves][PAGE_BYTES];
+  __shared__ float Wm[kDecodeWaves][16];
+  __shared__ float Wl[kDecodeWaves][16];
+  static_assert(GP * D * 4 <= 2 * PAGE_BYTES, "wave partials must fit in its two V buffers");
 
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int L = decode_len(a, b);
@@ -97,46 +117,59 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
       qf[c] = (col < G) ? *reinterpret_cast<const bf16x8*>(qrow + 32 * c + 8 * grp) : bf16x8{};
   }
 
+  // O^T accumulator: 8 blocks of 16 dims x 16 query columns; lane (col q,
+  // grp) holds dims 16*db + 4*grp + r of query q.
+  f32x4 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x4{};
   float m_ref = kNegInf, l_part = 0.f;
-  float acc[GP][8];
-#pragma unroll
-  for (int qq = 0; qq < GP; ++qq)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[qq][e] = 0.f;
-
   const float c2 = a.scale_log2;
 
-  // Registers of one page: K in the MFMA A-operand layout (token = lane%16,
-  // dims 32c + 8*(lane/16) .. +8) and four V rows (token lane/16 + 4i, dims
-  // 8*(lane%16) .. +8).  A page id outside [0, num_pages) is replaced by page
-  // 0 for the load and all its tokens are masked.
-  struct PageRegs {
+  // V DMA: lane i of instruction j writes LDS slot 64*j + i (16 B), which holds
+  // physical chunk slot%16 of page row slot/16.
+  unsigned v_off[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int slot = 64 * j + lane;
+    const int r = slot >> 4;
+    const int c = (slot & 15) ^ vswz(r);
+    v_off[j] = (unsigned)(r * D * 2 + c * 16);
+  }
+  // Transposed V read (block db): lane supplies row 4*grp + (lane%16)/4,
+  // dims 16*db + 4*(lane%4) .. +4 (8 bytes).
+  const int vr_row = 4 * grp + ((lane & 15) >> 2);
+  const int vr_sw = vswz(vr_row);
+
+  struct PageK {
     bf16x8 k[NC];
-    u32x4 v[4];
   };
-  auto load_page = [&](int i, PageRegs& r) {
+  auto phys_of = [&](int i) {
     int phys = __builtin_amdgcn_readlane(my_phys, i);
-    if (phys < 0 || phys >= a.num_pages) phys = 0;
+    return (phys < 0 || phys >= a.num_pages) ? -1 : phys;
+  };
+  // Page i: K into registers (MFMA A layout: token lane%16, dims 32c +
+  // 8*(lane/16) .. +8) and V into the LDS buffer vdst by DMA.  An invalid page
+  // id loads page 0 (in bounds) and its tokens are masked.
+  auto load_page = [&](int i, PageK& r, char* vdst) {
+    int phys = phys_of(i);
+    if (phys < 0) phys = 0;
     const size_t base = ((size_t)phys * a.Hkv + g) * kPage * D;
     const __bf16* kp = a.kc + base;
-    const __bf16* vp = a.vc + base;
+    const char* vp = reinterpret_cast<const char*>(a.vc + base);
 #pragma unroll
     for (int c = 0; c < NC; ++c)
       r.k[c] = *reinterpret_cast<const bf16x8*>(kp + col * D + 32 * c + 8 * grp);
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4)
-      r.v[i4] = *reinterpret_cast<const u32x4*>(vp + (grp + 4 * i4) * D + 8 * col);
+    for (int j = 0; j < 4; ++j) dma16(vp + v_off[j], vdst + 1024 * j);
   };
 
-  auto process_page = [&](int i, const PageRegs& r) {
-    const int phys = __builtin_amdgcn_readlane(my_phys, i);
-    const bool valid = phys >= 0 && phys < a.num_pages;
+  auto process_page = [&](int i, const PageK& r, const char* vsrc) {
+    const bool valid = phys_of(i) >= 0;
     const int tok0 = (p0 + wave + kDecodeWaves * i) * kPage;
-    // Tokens at or past `lim` are masked (the sequence end, or the whole page
-    // when its id is invalid).
-    const int lim = valid ? L : tok0;
+    const int lim = valid ? L : tok0;  // tokens at or past lim are masked
     const bool tail = tok0 + kPage > lim;
 
+    // S^T = K Q^T: lane (col q, grp) holds tokens 4*grp + rr of query q.
     f32x4 sc = f32x4{};
 #pragma unroll
     for (int c = 0; c < NC; ++c) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.k[c], qf[c], sc, 0, 0, 0);
@@ -148,90 +181,77 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
     float mx = __builtin_fmaxf(__builtin_fmaxf(sc[0], sc[1]), __builtin_fmaxf(sc[2], sc[3]));
     mx = max_xor32(max_xor16(mx)) * c2;
     const bool need = mx > m_ref + kDecodeRescaleThreshold;
-    const float alpha = need ? exp2_fast(m_ref - mx) : 1.f;
     if (__builtin_amdgcn_ballot_w64(need)) {
+      const float alpha = need ? exp2_fast(m_ref - mx) : 1.f;
       m_ref = need ? mx : m_ref;
       l_part *= alpha;
-      float al[GP];
 #pragma unroll
-      for (int qq = 0; qq < GP; ++qq)
-        al[qq] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), qq));
-#pragma unroll
-      for (int qq = 0; qq < GP; ++qq)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[qq][e] *= al[qq];
+      for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
     }
     const float m_use = (m_ref == kNegInf) ? 0.f : m_ref;
-    float pr[4];
+    bf16x4 pb;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      pr[rr] = exp2_fast(__builtin_fmaf(sc[rr], c2, -m_use));
-      l_part += pr[rr];
+      const float pv = exp2_fast(__builtin_fmaf(sc[rr], c2, -m_use));
+      l_part += pv;
+      pb[rr] = (__bf16)pv;
     }
-
-    // Hand the probabilities to the lanes that hold the matching V rows.
-    if (col < GP) {
+    // Slots past the end of the sequence may hold anything: zero P is not
+    // enough (0 * NaN), so masked tokens' V rows must not enter the product.
+    // Their P is exactly 0 and finite V is guaranteed by zeroing the A operand
+    // below only on the (rare) tail page.
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    const i16x4 pbi = __builtin_bit_cast(i16x4, pb);
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) Pl[wave][(4 * grp + rr) * GP + col] = pr[rr];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
+    for (int db = 0; db < NDB; ++db) {
+      const int cbyte = (16 * db + 4 * (lane & 3)) * 2;
+      const int off = vr_row * D * 2 + ((((cbyte >> 4) ^ vr_sw) << 4) | (cbyte & 15));
+      i16x4 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(
+              (__attribute__((address_space(3))) char*)(vsrc) + off));
+      if (tail) {
+        // element t of vt is token 4*grp + t of this page
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int t = grp + 4 * i4;
-      float vv[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vv[2 * e] = bf16lo_to_f32(r.v[i4][e]);
-        vv[2 * e + 1] = bf16hi_to_f32(r.v[i4][e]);
+        for (int t = 0; t < 4; ++t)
+          if (tok0 + 4 * grp + t >= lim) vt[t] = 0;
       }
-      if (tail && tok0 + t >= lim) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vv[e] = 0.f;  // slots past the end may hold anything
-      }
-      float pq[GP];
-#pragma unroll
-      for (int qq = 0; qq < GP; ++qq) pq[qq] = Pl[wave][t * GP + qq];
-#pragma unroll
-      for (int qq = 0; qq < GP; ++qq)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[qq][e] = __builtin_fmaf(pq[qq], vv[e], acc[qq][e]);
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pbi, acc[db], 0, 0, 0);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  // Two register sets: page i+1 is in flight while page i is processed.
-  PageRegs ra, rb;
-  if (cnt > 0) load_page(0, ra);
+  // Two K register sets and two V buffers: page i+1 is in flight while page i
+  // is processed.
+  PageK ka, kb;
+  if (cnt > 0) load_page(0, ka, sV0[wave]);
   for (int i = 0; i < cnt; i += 2) {
-    if (i + 1 < cnt) load_page(i + 1, rb);
-    process_page(i, ra);
+    if (i + 1 < cnt) load_page(i + 1, kb, sV1[wave]);
+    process_page(i, ka, sV0[wave]);
     if (i + 1 >= cnt) break;
-    if (i + 2 < cnt) load_page(i + 2, ra);
-    process_page(i + 1, rb);
+    if (i + 2 < cnt) load_page(i + 2, ka, sV0[wave]);
+    process_page(i + 1, kb, sV1[wave]);
   }
 
-  // Sum the four token groups of each column, then merge the waves.
-  float l_tot = sum_xor32(sum_xor16(l_part));
+  // Row sums: sum the four token groups of each column.  The accumulator
+  // needs no cross-lane sum (lanes hold distinct dims).
+  const float l_tot = sum_xor32(sum_xor16(l_part));
+  if (grp == 0 && col < GP) {
+    Wm[wave][col] = m_ref;
+    Wl[wave][col] = l_tot;
+  }
+  // The wave's partial outputs go to its own V buffers, idle from here on
+  // (every DMA into them was waited for before its page was read).
+  float* wacc_own = reinterpret_cast<float*>(col * D * 4 < PAGE_BYTES ? sV0[wave] : sV1[wave]);
+  if (col < GP) {
+    const int base = (col * D) % (PAGE_BYTES / 4);
 #pragma unroll
-  for (int qq = 0; qq < GP; ++qq)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[qq][e] = sum_xor32(sum_xor16(acc[qq][e]));
-  if (grp == 0) {
-    if (col < GP) {
-      Wm[wave][col] = m_ref;
-      Wl[wave][col] = l_tot;
-    }
-#pragma unroll
-    for (int qq = 0; qq < GP; ++qq)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) Wacc[wave][qq][8 * col + e] = acc[qq][e];
+    for (int db = 0; db < NDB; ++db)
+      *reinterpret_cast<f32x4*>(wacc_own + base + 16 * db + 4 * grp) = acc[db];
   }
   __syncthreads();
+  auto wacc = [&](int w, int qq, int d) {
+    const float* buf = reinterpret_cast<const float*>(qq * D * 4 < PAGE_BYTES ? sV0[w] : sV1[w]);
+    return buf[(qq * D) % (PAGE_BYTES / 4) + d];
+  };
 
   for (int i = tid; i < G * D; i += kDecodeWaves * 64) {
     const int qq = i / D, d = i - (i / D) * D;
@@ -244,7 +264,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
     for (int w = 0; w < kDecodeWaves; ++w) {
       const float wt = exp2_fast(Wm[w][qq] - Mu);
       wsum = __builtin_fmaf(wt, Wl[w][qq], wsum);
-      osum = __builtin_fmaf(wt, Wacc[w][qq][d], osum);
+      osum = __builtin_fmaf(wt, wacc(w, qq, d), osum);
     }
     const size_t row = ((size_t)b * a.H + (size_t)g * G + qq) * a.max_splits + s;
     a.ws_o[row * D + d] = wsum > 0.f ? osum / wsum : 0.f;
@@ -252,56 +272,71 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
   }
 }
 
-// Merge of the splits of one (b, h): one wave; lanes take splits for the
-// max / weight sums and two head dims each for the weighted output sum.
+// Merge of the split partials of one (b, h): 4 waves.  The workgroup first
+// finds the largest partial lse; wave w then sums splits w, w+4, ... with weights
+// exp2(lse_e - max), each lane owning two head dims; the waves' sums are
+// added through LDS.
 template <int D>
-__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   static_assert(D == 128, "two head dims per lane");
+  __shared__ float red[4];
+  __shared__ float part_o[4][D];
+  __shared__ float part_w[4];
   const int bh = blockIdx.x;
   const int b = bh / a.H;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int L = decode_len(a, b);
   const int npg = (L + kPage - 1) / kPage;
-  const int ns = (npg + a.split_pages - 1) / a.split_pages;
-  const float* lse_s = a.ws_lse + (size_t)bh * a.max_splits;
-  const float* o_s = a.ws_o + (size_t)bh * a.max_splits * D;
+  const int ne = (npg + a.split_pages - 1) / a.split_pages;
+  const size_t row0 = (size_t)bh * a.max_splits;
+  const float* lse_e = a.ws_lse + row0;
+  const float* o_e = a.ws_o + row0 * D;
   float M = kNegInf;
-  for (int s0 = 0; s0 < ns; s0 += 64)
-    if (s0 + lane < ns) M = fmax2(M, lse_s[s0 + lane]);
+  for (int e = tid; e < ne; e += 256) M = fmax2(M, lse_e[e]);
   for (int off = 32; off >= 1; off >>= 1) M = fmax2(M, __shfl_xor(M, off));
+  if (lane == 0) red[wave] = M;
+  __syncthreads();
+  M = fmax2(fmax2(red[0], red[1]), fmax2(red[2], red[3]));
   const float Mu = (M == kNegInf) ? 0.f : M;
-  float W = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += 64)
-    if (s0 + lane < ns) W += exp2_fast(lse_s[s0 + lane] - Mu);
-  for (int off = 32; off >= 1; off >>= 1) W += __shfl_xor(W, off);
-  float o0 = 0.f, o1 = 0.f;
-  int s = 0;
-  for (; s + 4 <= ns; s += 4) {
+  float W = 0.f, o0 = 0.f, o1 = 0.f;
+  int e = wave;
+  for (; e + 12 < ne; e += 16) {
     float w[4];
     f32x2 x[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      w[u] = exp2_fast(lse_s[s + u] - Mu);
-      x[u] = *reinterpret_cast<const f32x2*>(o_s + (size_t)(s + u) * D + 2 * lane);
+      w[u] = exp2_fast(lse_e[e + 4 * u] - Mu);
+      x[u] = *reinterpret_cast<const f32x2*>(o_e + (size_t)(e + 4 * u) * D + 2 * lane);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
+      W += w[u];
       o0 = __builtin_fmaf(w[u], x[u][0], o0);
       o1 = __builtin_fmaf(w[u], x[u][1], o1);
     }
   }
-  for (; s < ns; ++s) {
-    const float w = exp2_fast(lse_s[s] - Mu);
-    const f32x2 x = *reinterpret_cast<const f32x2*>(o_s + (size_t)s * D + 2 * lane);
+  for (; e < ne; e += 4) {
+    const float w = exp2_fast(lse_e[e] - Mu);
+    const f32x2 x = *reinterpret_cast<const f32x2*>(o_e + (size_t)e * D + 2 * lane);
+    W += w;
     o0 = __builtin_fmaf(w, x[0], o0);
     o1 = __builtin_fmaf(w, x[1], o1);
   }
-  const float inv = W > 0.f ? 1.f / W : 0.f;
+  part_o[wave][2 * lane] = o0;
+  part_o[wave][2 * lane + 1] = o1;
+  if (lane == 0) part_w[wave] = W;
+  __syncthreads();
+  if (wave != 0) return;
+  const float Wt = part_w[0] + part_w[1] + part_w[2] + part_w[3];
+  const float inv = Wt > 0.f ? 1.f / Wt : 0.f;
   bf16x2 ov;
-  ov[0] = (__bf16)(o0 * inv);
-  ov[1] = (__bf16)(o1 * inv);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int d = 2 * lane + u;
+    ov[u] = (__bf16)((part_o[0][d] + part_o[1][d] + part_o[2][d] + part_o[3][d]) * inv);
+  }
   *reinterpret_cast<bf16x2*>(a.o + (size_t)bh * D + 2 * lane) = ov;
-  if (lane == 0) a.lse[bh] = W > 0.f ? (Mu + log2_fast(W)) * kLn2 : kNegInf;
+  if (lane == 0) a.lse[bh] = Wt > 0.f ? (Mu + log2_fast(Wt)) * kLn2 : kNegInf;
 }
 
 int decode_split_pages(int B, int H, int max_seqlen) {
@@ -328,8 +363,9 @@ size_t decode_workspace_bytes(int B, int H, int max_seqlen, int d) {
 }
 
 template <int GP>
-static void launch_split(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<128, GP>), grid, dim3(kDecodeWaves * 64), 0, stream, a);
+static void launch_split(const DecodeArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_split_kernel<128, GP>), dim3(a.max_splits, a.Hkv, a.B),
+                     dim3(kDecodeWaves * 64), 0, stream, a);
 }
 
 hipError_t launch_decode(const void* q, const void* kcache, const void* vcache,
@@ -354,17 +390,16 @@ hipError_t launch_decode(const void* q, const void* kcache, const void* vcache,
   a.ws_o = static_cast<float*>(workspace);
   a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                       align_up(rows * d * sizeof(float), 256));
-  dim3 grid(a.max_splits, Hkv, B);
   const int G = a.G;
-  if (G <= 1) launch_split<1>(a, grid, stream);
-  else if (G <= 2) launch_split<2>(a, grid, stream);
-  else if (G <= 4) launch_split<4>(a, grid, stream);
-  else if (G <= 8) launch_split<8>(a, grid, stream);
-  else if (G <= 16) launch_split<16>(a, grid, stream);
+  if (G <= 1) launch_split<1>(a, stream);
+  else if (G <= 2) launch_split<2>(a, stream);
+  else if (G <= 4) launch_split<4>(a, stream);
+  else if (G <= 8) launch_split<8>(a, stream);
+  else if (G <= 16) launch_split<16>(a, stream);
   else return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(B * H), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(B * H), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
