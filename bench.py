@@ -75,6 +75,63 @@ def measured_traffic(kernel_key: str, src_hash: str):
     return rec.get("bytes_per_launch")
 
 
+KERNEL_KEYS = {  # traffic.json key -> (kernel-name fragments, sources)
+    "prefill_bf16": (("prefill_bf16_kernel<128",), ("prefill_bf16.hip", "common.hpp")),
+    "decode": (("decode_split_kernel<128, 4>", "decode_combine_kernel"), ("decode.hip", "common.hpp")),
+}
+CALIBRATION_COPY_BYTES = 256 << 20
+
+
+def traffic_from_counters(fetch_csv: str, write_csv: str) -> dict:
+    """HBM bytes per launch from two rocprofv3 --pmc CSVs (FETCH_SIZE, then
+    WRITE_SIZE; KiB per dispatch).  Each counter is scaled by the ratio of the
+    known size of the 256 MiB calibration copy to what the counter read for
+    that copy.  Multi-kernel entries (decode) sum their kernels per launch."""
+    import csv
+    from collections import defaultdict
+
+    def per_kernel(path, counter):
+        vals = defaultdict(list)
+        calib = []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name, v = r["Kernel_Name"], float(r["Counter_Value"])
+            if "copyBuffer" in name and int(r["Grid_Size"]) >= 65536:
+                calib.append(v)
+            vals[name].append(v)
+        return vals, calib
+
+    out = {"_about": "HBM traffic per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE "
+                     "(KiB per dispatch), each scaled by known/measured bytes of a 256 MiB "
+                     "device copy in the same run; valid only for the recorded source hash."}
+    scale = {}
+    vals = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        v, calib = per_kernel(path, counter)
+        if not calib:
+            raise SystemExit(f"no calibration copy in {path}")
+        scale[counter] = CALIBRATION_COPY_BYTES / (1024.0 * (sum(calib) / len(calib)))
+        vals[counter] = v
+    out["scale"] = {k: round(x, 5) for k, x in scale.items()}
+    for key, (frags, srcs) in KERNEL_KEYS.items():
+        rec = {"source_hash": source_hash(*srcs)}
+        total = 0.0
+        for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+            kib = 0.0
+            for frag in frags:
+                hits = [x for name, xs in vals[counter].items() if frag in name for x in xs]
+                if not hits:
+                    raise SystemExit(f"{frag} not in the {counter} run")
+                kib += sum(hits) / len(hits)
+            rec[counter.lower() + "_kib_raw"] = round(kib, 1)
+            rec[counter.lower() + "_bytes"] = int(kib * 1024 * scale[counter])
+            total += kib * 1024 * scale[counter]
+        rec["bytes_per_launch"] = int(total)
+        out[key] = rec
+    return out
+
+
 def cpu_baseline(inp, rows_per_head: int, heads: list[int]):
     """The oracle, as it is, on a bounded sample: `rows_per_head` evenly
     spread rows of the given heads of the prefill workload."""
@@ -103,6 +160,52 @@ def cpu_baseline(inp, rows_per_head: int, heads: list[int]):
                       f"{dt:.1f} s wall; in-band FLOPs of those rows only"}
 
 
+OTHER_WORKLOADS = [  # name, B, H, Hkv, n, d, causal, window, dtype, seed
+    ("single-head fp32 full n256 d64", 1, 1, 1, 256, 64, 0, -1, "f32", 1),
+    ("causal MHA B4 H16 n4096 d128 bf16", 4, 16, 16, 4096, 128, 1, -1, "bf16", 2),
+    ("band |i-j|<=2048 B1 H32 n32768 d128 bf16", 1, 32, 32, 32768, 128, 0, 2048, "bf16", 3),
+]
+
+
+def time_other_workloads(fa, torch, np, bf, stream, reps: int = 20):
+    """Average kernel time (HIP events) of the other prefill workloads."""
+    from io_aware_exact_fa_amd.inputs import prefill_inputs
+    res = []
+    for name, B, H, Hkv, n, d, causal, window, dt, seed in OTHER_WORKLOADS:
+        inp = prefill_inputs(B, H, Hkv, n, d, seed=seed, dtype=dt)
+        if dt == "bf16":
+            q, k, v = bf(inp["q_bits"]), bf(inp["k_bits"]), bf(inp["v_bits"])
+            dtype = fa.FA_BF16
+        else:
+            q, k, v = (torch.from_numpy(inp[x]).cuda() for x in ("q", "k", "v"))
+            dtype = fa.FA_F32
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, n), dtype=torch.float32, device=q.device)
+        f = lambda: fa.fa_fwd(q, k, v, o, lse, B, H, Hkv, n, d, causal, window,
+                              1.0 / math.sqrt(d), dtype, stream)
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        flops = 4 * d * inband_pairs(n, bool(causal), window) * B * H
+        tf = flops / (ms * 1e-3) / 1e12
+        rec = {"workload": name, "ms": round(ms, 4), "TFLOP/s": round(tf, 2)}
+        if dt == "bf16":
+            rec["frac_of_bf16_peak"] = round(tf / PEAK_BF16_TFLOPS, 4)
+        log(f"{name}: {ms:.4f} ms  {tf:.1f} TFLOP/s in-band")
+        res.append(rec)
+        del q, k, v, o, lse
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -110,7 +213,21 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-rows", type=int, default=16384,
                     help="query rows per sampled head for the oracle baseline (>= 1)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc runs and exit "
+                         "(no GPU needed)")
+    ap.add_argument("--all-workloads", action="store_true",
+                    help="also time every workload (fp32 n=256, causal n=4096, band n=32768) "
+                         "and print one line each to stderr")
     args = ap.parse_args()
+    if args.traffic_from:
+        rec = traffic_from_counters(*args.traffic_from)
+        path = os.path.join(ROOT, "profiles", "traffic.json")
+        with open(path, "w") as f:
+            json.dump(rec, f, indent=2)
+            f.write("\n")
+        print(json.dumps(rec, indent=2))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): this build "
               "has no multi-GPU path", file=sys.stderr)
@@ -242,6 +359,8 @@ def main():
     }
     del q, k, v, o, dq, dk, dv
     torch.cuda.empty_cache()
+    if args.all_workloads:
+        out["other_workloads"] = time_other_workloads(fa, torch, np, bf, stream)
     log("timing the oracle on a bounded sample")
     out["cpu_baseline"] = cpu_baseline(pin, max(1, args.cpu_rows),
                                        heads=[0, 5, 10, 15, 16, 21, 26, 31])
