@@ -30,3 +30,4 @@ from .attention import (  # noqa: F401
     decode_fwd,
     gather_paged_kv,
 )
+from .attention_bwd import attention_bwd, probabilities  # noqa: F401

@@ -80,8 +80,8 @@ def test_hand_cases():
     d = 4
     q, k, v = _rand(rng, 1, 1, 1, d), _rand(rng, 1, 1, 1, d), _rand(rng, 1, 1, 1, d)
     o, lse = attention_fwd(q, k, v, False, -1, 0.5)
-    np.testing.assert_allclose(o[0, 0, 0], v[0, 0, 0], atol=1e-15)
-    np.testing.assert_allclose(lse[0, 0, 0], 0.5 * q[0, 0, 0] @ k[0, 0, 0], atol=1e-15)
+    np.testing.assert_allclose(o[0, 0, 0], v[0, 0, 0], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse[0, 0, 0], 0.5 * q[0, 0, 0] @ k[0, 0, 0], rtol=0, atol=1e-15)
     # n = 2: a two-way softmax is a logistic sigmoid of the score difference.
     q, k, v = _rand(rng, 1, 1, 2, d), _rand(rng, 1, 1, 2, d), _rand(rng, 1, 1, 2, d)
     o, lse = attention_fwd(q, k, v, False, -1, 1.0)
@@ -90,8 +90,8 @@ def test_hand_cases():
         s1 = q[0, 0, i] @ k[0, 0, 1]
         w0 = 1.0 / (1.0 + math.exp(s1 - s0))
         np.testing.assert_allclose(o[0, 0, i], w0 * v[0, 0, 0] + (1 - w0) * v[0, 0, 1],
-                                   atol=1e-14)
-        np.testing.assert_allclose(lse[0, 0, i], np.logaddexp(s0, s1), atol=1e-14)
+                                   rtol=0, atol=1e-14)
+        np.testing.assert_allclose(lse[0, 0, i], np.logaddexp(s0, s1), rtol=0, atol=1e-14)
 
 
 # --------------------------------------------------------------------------
@@ -147,7 +147,7 @@ def test_probability_rows(causal, window):
     mask = visible_mask(np.arange(n), n, causal, window)
     assert np.all(p >= 0)
     assert np.all(p[~mask] == 0)
-    np.testing.assert_allclose(p.sum(axis=1), 1.0, atol=1e-14)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-14)
 
 
 @pytest.mark.parametrize("causal,window", MODES)
@@ -158,12 +158,12 @@ def test_constant_and_linear_in_v(causal, window):
     c = rng.standard_normal(d)
     v_const = np.broadcast_to(c, (1, 2, n, d)).copy()
     o, _ = attention_fwd(q, k, v_const, causal, window, 0.4)
-    np.testing.assert_allclose(o, np.broadcast_to(c, o.shape), atol=1e-14)
+    np.testing.assert_allclose(o, np.broadcast_to(c, o.shape), rtol=0, atol=1e-14)
     v1, v2 = _rand(rng, 1, 2, n, d), _rand(rng, 1, 2, n, d)
     o1, _ = attention_fwd(q, k, v1, causal, window, 0.4)
     o2, _ = attention_fwd(q, k, v2, causal, window, 0.4)
     o12, _ = attention_fwd(q, k, 2.5 * v1 - 0.75 * v2, causal, window, 0.4)
-    np.testing.assert_allclose(o12, 2.5 * o1 - 0.75 * o2, atol=1e-13)
+    np.testing.assert_allclose(o12, 2.5 * o1 - 0.75 * o2, rtol=0, atol=1e-13)
 
 
 @pytest.mark.parametrize("causal,window", MODES)
@@ -176,8 +176,8 @@ def test_key_shift(causal, window):
     c = rng.standard_normal(d)
     o, lse = attention_fwd(q, k, v, causal, window, scale)
     o2, lse2 = attention_fwd(q, k + c, v, causal, window, scale)
-    np.testing.assert_allclose(o2, o, atol=1e-13)
-    np.testing.assert_allclose(lse2 - lse, scale * (q[0, 0] @ c)[None, None], atol=1e-13)
+    np.testing.assert_allclose(o2, o, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse2 - lse, scale * (q[0, 0] @ c)[None, None], rtol=0, atol=1e-13)
 
 
 def test_full_mode_permutation_equivariance():
@@ -187,8 +187,8 @@ def test_full_mode_permutation_equivariance():
     perm = rng.permutation(n)
     o, lse = attention_fwd(q, k, v, False, -1, 0.3)
     o2, lse2 = attention_fwd(q, k[:, :, perm], v[:, :, perm], False, -1, 0.3)
-    np.testing.assert_allclose(o2, o, atol=1e-14)
-    np.testing.assert_allclose(lse2, lse, atol=1e-14)
+    np.testing.assert_allclose(o2, o, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse2, lse, rtol=0, atol=1e-14)
 
 
 # --------------------------------------------------------------------------
@@ -205,8 +205,8 @@ def test_window_covering_sequence(n):
         for causal in (False, True):
             a = attention_fwd(q, k, v, causal, w, 0.35)
             b = attention_fwd(q, k, v, causal, -1, 0.35)
-            np.testing.assert_allclose(a[0], b[0], atol=0)
-            np.testing.assert_allclose(a[1], b[1], atol=0)
+            np.testing.assert_allclose(a[0], b[0], rtol=0, atol=0)
+            np.testing.assert_allclose(a[1], b[1], rtol=0, atol=0)
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -216,9 +216,9 @@ def test_window_zero(causal):
     rng = np.random.default_rng(15)
     q, k, v = _rand(rng, 1, 1, n, d), _rand(rng, 1, 1, n, d), _rand(rng, 1, 1, n, d)
     o, lse = attention_fwd(q, k, v, causal, 0, scale)
-    np.testing.assert_allclose(o, v, atol=1e-15)
+    np.testing.assert_allclose(o, v, rtol=0, atol=1e-15)
     np.testing.assert_allclose(lse[0, 0], scale * np.einsum("id,id->i", q[0, 0], k[0, 0]),
-                               atol=1e-14)
+                               rtol=0, atol=1e-14)
 
 
 def _closed_form_count(i, n, causal, window):
@@ -242,8 +242,8 @@ def test_zero_query_gives_mean_and_log_count(causal, window):
         cnt = _closed_form_count(i, n, causal, window)
         js = list(_visible_range(i, n, causal, window))
         assert len(js) == cnt
-        np.testing.assert_allclose(lse[0, 0, i], math.log(cnt), atol=1e-14)
-        np.testing.assert_allclose(o[0, 0, i], v[0, 0, js].mean(axis=0), atol=1e-14)
+        np.testing.assert_allclose(lse[0, 0, i], math.log(cnt), rtol=0, atol=1e-14)
+        np.testing.assert_allclose(o[0, 0, i], v[0, 0, js].mean(axis=0), rtol=0, atol=1e-14)
 
 
 def test_gqa_equals_repeated_kv():
@@ -254,8 +254,8 @@ def test_gqa_equals_repeated_kv():
     a = attention_fwd(q, k, v, True, 9, 0.3)
     b = attention_fwd(q, np.repeat(k, H // Hkv, axis=1), np.repeat(v, H // Hkv, axis=1),
                       True, 9, 0.3)
-    np.testing.assert_allclose(a[0], b[0], atol=0)
-    np.testing.assert_allclose(a[1], b[1], atol=0)
+    np.testing.assert_allclose(a[0], b[0], rtol=0, atol=0)
+    np.testing.assert_allclose(a[1], b[1], rtol=0, atol=0)
 
 
 def test_rows_subset_and_workers_match_full():
@@ -265,8 +265,8 @@ def test_rows_subset_and_workers_match_full():
     o, lse = attention_fwd(q, k, v, True, 20, 0.3)
     rows = np.array([0, 5, 69, 33, 34])
     o2, lse2 = attention_fwd(q, k, v, True, 20, 0.3, rows=rows, workers=2, chunk=2)
-    np.testing.assert_allclose(o2, o[:, :, rows], atol=0)
-    np.testing.assert_allclose(lse2, lse[:, :, rows], atol=0)
+    np.testing.assert_allclose(o2, o[:, :, rows], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse2, lse[:, :, rows], rtol=0, atol=1e-14)
 
 
 # --------------------------------------------------------------------------
@@ -313,14 +313,14 @@ def test_decode_matches_brute_and_last_causal_row():
         qq = np.zeros((H, L, d))
         qq[:, L - 1] = q[b]
         ob, lb = _brute(qq.tolist(), kb.tolist(), vb.tolist(), True, -1, 0.5)
-        np.testing.assert_allclose(o[b], np.array(ob)[:, L - 1], atol=1e-13)
-        np.testing.assert_allclose(lse[b], np.array(lb)[:, L - 1], atol=1e-13)
+        np.testing.assert_allclose(o[b], np.array(ob)[:, L - 1], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lse[b], np.array(lb)[:, L - 1], rtol=0, atol=1e-13)
         # the last row of a causal prefill over the gathered cache
         qf = np.zeros((1, H, L, d))
         qf[0, :, L - 1] = q[b]
         of, lf = attention_fwd(qf, kb[None], vb[None], True, -1, 0.5, rows=[L - 1])
-        np.testing.assert_allclose(o[b], of[0, :, 0], atol=1e-14)
-        np.testing.assert_allclose(lse[b], lf[0, :, 0], atol=1e-14)
+        np.testing.assert_allclose(o[b], of[0, :, 0], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(lse[b], lf[0, :, 0], rtol=0, atol=1e-14)
 
 
 def test_decode_page_permutation_invariance():
@@ -389,5 +389,5 @@ def test_attention_rows_direct():
     q, k, v = _rand(rng, 1, 1, 9, 4), _rand(rng, 1, 1, 9, 4), _rand(rng, 1, 1, 9, 4)
     o, lse = attention_fwd(q, k, v, True, 2, 0.5)
     o2, lse2 = attention_rows(q[0, 0, [3, 8]], k[0, 0], v[0, 0], [3, 8], True, 2, 0.5)
-    np.testing.assert_allclose(o2, o[0, 0, [3, 8]], atol=0)
-    np.testing.assert_allclose(lse2, lse[0, 0, [3, 8]], atol=0)
+    np.testing.assert_allclose(o2, o[0, 0, [3, 8]], rtol=0, atol=0)
+    np.testing.assert_allclose(lse2, lse[0, 0, [3, 8]], rtol=0, atol=0)

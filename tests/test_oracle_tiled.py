@@ -27,8 +27,8 @@ def test_tiled_equals_oracle(block, causal, window):
     b = n if block == "n" else block
     o_t, l_t, _ = tiled_attention(q, k, v, b, causal, window, 0.25)
     o, lse = attention_fwd(q[None, None], k[None, None], v[None, None], causal, window, 0.25)
-    np.testing.assert_allclose(o_t, o[0, 0], atol=1e-12)
-    np.testing.assert_allclose(l_t, lse[0, 0], atol=1e-12)
+    np.testing.assert_allclose(o_t, o[0, 0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l_t, lse[0, 0], rtol=0, atol=1e-12)
 
 
 @pytest.mark.parametrize("n,w,block", [(256, 100, 64), (300, 37, 64), (256, 64, 64),
@@ -41,11 +41,11 @@ def test_skip_is_exact(n, w, block):
     for causal in (False, True):
         a = tiled_attention(q, k, v, block, causal, w, 0.3, skip=True)
         b = tiled_attention(q, k, v, block, causal, w, 0.3, skip=False)
-        np.testing.assert_allclose(a[0], b[0], atol=1e-13)
-        np.testing.assert_allclose(a[1], b[1], atol=1e-13)
+        np.testing.assert_allclose(a[0], b[0], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(a[1], b[1], rtol=0, atol=1e-13)
         assert not np.isnan(a[0]).any()
         o, lse = attention_fwd(q[None, None], k[None, None], v[None, None], causal, w, 0.3)
-        np.testing.assert_allclose(a[0], o[0, 0], atol=1e-12)
+        np.testing.assert_allclose(a[0], o[0, 0], rtol=0, atol=1e-12)
         assert a[2] <= b[2]
 
 
@@ -99,5 +99,5 @@ def test_split_merge_equals_decode_oracle(cuts):
     kflat = kc[:, 0].reshape(-1, d)[:L]
     vflat = vc[:, 0].reshape(-1, d)[:L]
     o_m, lse_m = split_merge_attention(q[0, 0], kflat, vflat, cuts, 0.4)
-    np.testing.assert_allclose(o_m, o[0, 0], atol=1e-13)
-    np.testing.assert_allclose(lse_m, lse[0, 0], atol=1e-13)
+    np.testing.assert_allclose(o_m, o[0, 0], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse_m, lse[0, 0], rtol=0, atol=1e-13)
