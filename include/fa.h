@@ -1,7 +1,8 @@
 /*
- * fa.h -- C ABI of libfa.so: exact attention forward for AMD MI355X (gfx950).
+ * fa.h -- C ABI of libfa.so: exact attention (forward, decode, backward) for
+ * AMD MI355X (gfx950).
  *
- * Two operations, both exact (no approximation of the softmax):
+ * Three operations, all exact (no approximation of the softmax):
  *
  *   fa_fwd     prefill / self-attention forward over a whole sequence, computed
  *              tile by tile with an online softmax so the n x n score matrix
@@ -10,6 +11,8 @@
  *   fa_decode  one new query token per sequence attending to its whole paged
  *              KV cache, split along the cache (flash decoding) and merged by
  *              log-sum-exp weights.
+ *   fa_bwd     gradients dq, dk, dv of fa_fwd's output, recomputing the
+ *              probabilities tile by tile from the saved log-sum-exp.
  *
  * Sources (web pages on IO-aware exact attention):
  *   - charles2530 blog "算子与编译器：FlashAttention 与长上下文": §1 (the
@@ -54,7 +57,7 @@ typedef enum {
   FA_ERR_NULL = -1,        /* a required pointer is NULL                      */
   FA_ERR_SHAPE = -2,       /* sizes are out of range or inconsistent          */
   FA_ERR_UNSUPPORTED = -3, /* valid request this build does not implement     */
-  FA_ERR_WORKSPACE = -4,   /* decode workspace missing or too small           */
+  FA_ERR_WORKSPACE = -4,   /* workspace missing or too small                  */
   FA_ERR_LAUNCH = -5       /* the HIP runtime rejected a kernel launch        */
 } fa_status;
 
@@ -132,6 +135,44 @@ int fa_decode(const void* q, const void* kcache, const void* vcache,
               float* lse, int B, int H, int Hkv, int d, int num_pages,
               int page_size, int max_pages, int max_seqlen, float scale,
               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_bwd_workspace_bytes -- device workspace fa_bwd needs for these sizes
+ * (one float per query row: D_i = <dO_i, O_i>).  0 if out of range.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int n, int d);
+
+/*
+ * fa_bwd -- gradients of attention over whole sequences (the backward pass).
+ *
+ * The score and probability matrices are not read from anywhere: they are
+ * recomputed tile by tile from q, k and the forward pass's lse (xxqk.cn
+ * sliding-window prefill article §3.3; bomianfm.com Q&A "FlashAttention的原理是
+ * 什么？对Agent性能有何提升？" §一), and key tiles outside the band are skipped
+ * as in fa_fwd.  With P_ij = exp(scale q_i.k_j - lse_i) on the visible pairs
+ * (0 elsewhere) and D_i = <dO_i, O_i>:
+ *   dv = P^T dO,  dS = P o (dO v^T - D),  dq = scale dS k,  dk = scale dS^T q,
+ * dk and dv summed over the query heads that share a key/value head.
+ *
+ *   q, o, dout [B, H,   n, d]  bf16   (o and lse exactly as fa_fwd wrote them
+ *   k, v       [B, Hkv, n, d]  bf16    for the same q, k, v and mask)
+ *   lse        [B, H,   n]     float32 (natural log, as written by fa_fwd)
+ *   dq         [B, H,   n, d]  float32, written
+ *   dk, dv     [B, Hkv, n, d]  float32, written (not accumulated into)
+ *   workspace  device memory of at least fa_bwd_workspace_bytes(B, H, n, d)
+ *              bytes; contents on entry do not matter.
+ *
+ * causal and window select the visible keys exactly as in fa_fwd.  The
+ * result is deterministic (no atomics; fixed summation order).
+ * Limits: as fa_fwd; dtype must be FA_BF16.
+ * Errors: FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED (d not 64/128 or
+ * dtype not FA_BF16), FA_ERR_WORKSPACE, FA_ERR_LAUNCH.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const float* lse, const void* dout, float* dq, float* dk, float* dv,
+           int B, int H, int Hkv, int n, int d, int causal, int window,
+           float scale, int dtype, void* workspace, size_t workspace_bytes,
+           void* stream);
 
 /* Human-readable text of a status code (static storage, never NULL). */
 const char* fa_strerror(int status);

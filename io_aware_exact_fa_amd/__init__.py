@@ -1,4 +1,5 @@
-"""FlashAttention forward (prefill + paged flash-decoding) for MI355X / gfx950.
+"""Exact FlashAttention for MI355X / gfx950: prefill forward, paged
+flash-decoding and the backward pass.
 
 The compute path is the HIP library ``libfa.so`` built from ``csrc/``; this
 package is a thin ctypes binding over its C ABI (see ``include/fa.h``).
@@ -8,6 +9,6 @@ not been built.
 
 from .binding import (  # noqa: F401
     FA_BF16, FA_F32, FaError, lib, lib_path,
-    fa_fwd, fa_decode, fa_decode_workspace_bytes, fa_strerror, fa_version,
-    flash_attn_fwd, flash_decode,
+    fa_fwd, fa_decode, fa_decode_workspace_bytes, fa_bwd, fa_bwd_workspace_bytes,
+    fa_strerror, fa_version, flash_attn_fwd, flash_decode, flash_attn_bwd,
 )

@@ -51,6 +51,11 @@ def lib() -> ctypes.CDLL:
     L.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                             i32, i32, i32, f32, vp, sz, vp]
     L.fa_decode.restype = i32
+    L.fa_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    L.fa_bwd_workspace_bytes.restype = sz
+    L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                         i32, i32, i32, f32, i32, vp, sz, vp]
+    L.fa_bwd.restype = i32
     L.fa_strerror.argtypes = [i32]
     L.fa_strerror.restype = ctypes.c_char_p
     L.fa_version.argtypes = []
@@ -109,6 +114,22 @@ def fa_decode(q, kcache, vcache, page_table, seqlens, o, lse, B, H, Hkv, d,
                          _ptr(workspace), int(workspace_bytes), _stream(stream))
     if st != 0:
         raise FaError(st, "fa_decode")
+
+
+def fa_bwd_workspace_bytes(B, H, n, d) -> int:
+    return int(lib().fa_bwd_workspace_bytes(int(B), int(H), int(n), int(d)))
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, n, d, causal, window,
+           scale, dtype, workspace, workspace_bytes, stream=None) -> None:
+    """Raw C-ABI call; tensors or integer device addresses."""
+    st = lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                      _ptr(dq), _ptr(dk), _ptr(dv), int(B), int(H), int(Hkv),
+                      int(n), int(d), int(causal), int(window), float(scale),
+                      int(dtype), _ptr(workspace), int(workspace_bytes),
+                      _stream(stream))
+    if st != 0:
+        raise FaError(st, "fa_bwd")
 
 
 # ---------------------------------------------------------------------------
@@ -174,3 +195,38 @@ def flash_decode(q, kcache, vcache, page_table, seqlens, max_seqlen: int,
               ps, page_table.shape[1], max_seqlen, scale, workspace,
               workspace.numel() * workspace.element_size(), stream)
     return out, lse
+
+
+def flash_attn_bwd(q, k, v, o, lse, dout, causal: bool = False, window: int = -1,
+                   scale: float | None = None, workspace=None, stream=None):
+    """Gradients (dq, dk, dv) as float32 tensors for bf16 q/k/v/o/dout.
+
+    o and lse must be what flash_attn_fwd returned for the same q, k, v,
+    causal, window and scale.
+    """
+    import torch
+    _check_contig(q, k, v, o, lse, dout)
+    B, H, n, d = q.shape
+    Hkv = k.shape[1]
+    for t in (q, k, v, o, dout):
+        if t.dtype != torch.bfloat16:
+            raise ValueError("fa_bwd takes bf16 q, k, v, o and dout")
+    if tuple(k.shape) != (B, Hkv, n, d) or tuple(v.shape) != (B, Hkv, n, d):
+        raise ValueError("k and v must be [B, Hkv, n, d]")
+    if tuple(o.shape) != (B, H, n, d) or tuple(dout.shape) != (B, H, n, d):
+        raise ValueError("o and dout must be [B, H, n, d]")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, n):
+        raise ValueError("lse must be float32 [B, H, n]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nbytes = fa_bwd_workspace_bytes(B, H, n, d)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty((B, H, n, d), **f32)
+    dk = torch.empty((B, Hkv, n, d), **f32)
+    dv = torch.empty((B, Hkv, n, d), **f32)
+    fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, n, d, int(bool(causal)),
+           int(window), scale, FA_BF16, workspace,
+           workspace.numel() * workspace.element_size(), stream)
+    return dq, dk, dv

@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfa.so")
 
-SOURCES = ["fa_abi.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip"]
+SOURCES = ["fa_abi.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip", "backward.hip"]
 
 # Packed fp32 vector ops (v_pk_*_f32) are switched off for all device code.
 HIPCC_FLAGS = [

@@ -21,7 +21,7 @@ bool fits_i32(long long x) { return x >= 0 && x < (long long)INT_MAX; }
 
 extern "C" {
 
-int fa_version(void) { return (1 << 16) | 0; }
+int fa_version(void) { return (1 << 16) | 1; }
 
 const char* fa_strerror(int status) {
   switch (status) {
@@ -29,7 +29,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "sizes out of range or inconsistent";
     case FA_ERR_UNSUPPORTED: return "request not supported by this build";
-    case FA_ERR_WORKSPACE: return "decode workspace missing or too small";
+    case FA_ERR_WORKSPACE: return "workspace missing or too small";
     case FA_ERR_LAUNCH: return "kernel launch rejected by the HIP runtime";
     default: return "unknown status";
   }
@@ -81,6 +81,34 @@ int fa_decode(const void* q, const void* kcache, const void* vcache, const int32
   hipError_t e = fa::launch_decode(q, kcache, vcache, page_table, seqlens, o, lse, B, H, Hkv, d,
                                    num_pages, max_pages, max_seqlen, scale, workspace,
                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int n, int d) {
+  if (B < 1 || H < 1 || n < 1 || d < 1) return 0;
+  if (!fits_i32((long long)B * H) || !fits_i32((long long)n * d)) return 0;
+  return fa::bwd_workspace_bytes(B, H, n);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, float* dq, float* dk, float* dv, int B, int H, int Hkv, int n, int d,
+           int causal, int window, float scale, int dtype, void* workspace,
+           size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || Hkv < 1 || n < 1 || d < 1) return FA_ERR_SHAPE;
+  if (H % Hkv != 0) return FA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
+  if (!scale_ok(scale)) return FA_ERR_SHAPE;
+  if (!fits_i32((long long)n * d)) return FA_ERR_SHAPE;
+  if (!fits_i32((long long)B * H)) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < fa::bwd_workspace_bytes(B, H, n)) return FA_ERR_WORKSPACE;
+  if (window < 0) window = -1;
+  if (window > n) window = n;
+  hipError_t e = fa::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv,
+                                     static_cast<float*>(workspace), B, H, Hkv, n, d, causal,
+                                     window, scale, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -28,4 +28,11 @@ hipError_t launch_decode(const void* q, const void* kcache, const void* vcache,
                          int max_pages, int max_seqlen, float scale, void* workspace,
                          hipStream_t stream);
 
+// Backward: delta workspace [B,H,n] floats; window clamped as for prefill.
+size_t bwd_workspace_bytes(int B, int H, int n);
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                           float* delta, int B, int H, int Hkv, int n, int d, int causal,
+                           int window, float scale, hipStream_t stream);
+
 }  // namespace fa

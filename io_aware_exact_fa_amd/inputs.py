@@ -10,6 +10,9 @@ Recipe (fixed so every consumer sees bit-identical inputs):
   * prefill: Q, then K, then V are drawn in that order, each in [B, heads, n, d]
     C order; an optional ``draw_scale`` multiplies each float32 draw before
     rounding (0.5 is exact in binary floating point);
+  * backward: the output gradient dO [B, H, n, d] is drawn from
+    ``default_rng([seed, 3])`` (same draw_scale rule), so Q, K and V do not
+    move when it is added;
   * bf16 storage: round-to-nearest-even of the float32 draw to bfloat16;
     the returned float32 arrays hold exactly the rounded values;
   * decode: from ``default_rng(seed)``: the sequence lengths (discrete uniform
@@ -34,6 +37,7 @@ __all__ = [
     "bf16_round",
     "bf16_bits_to_f32",
     "prefill_inputs",
+    "grad_output",
     "decode_lengths_and_table",
     "decode_sequence_kv",
     "decode_inputs",
@@ -87,6 +91,15 @@ def prefill_inputs(B: int, H: int, Hkv: int, n: int, d: int, seed: int,
         else:
             raise ValueError(f"unknown dtype {dtype!r}")
     return out
+
+
+def grad_output(B: int, H: int, n: int, d: int, seed: int,
+                draw_scale: float = 1.0):
+    """Output gradient dO [B,H,n,d] for the backward pass, rounded to bf16.
+
+    Returns (float32 values holding the bf16 numbers, raw uint16 bits).
+    """
+    return bf16_round(_draw(np.random.default_rng([seed, 3]), (B, H, n, d), draw_scale))
 
 
 def decode_lengths_and_table(B: int, H: int, d: int, page_size: int,

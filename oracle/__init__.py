@@ -30,4 +30,9 @@ from .attention import (  # noqa: F401
     decode_fwd,
     gather_paged_kv,
 )
-from .attention_bwd import attention_bwd, probabilities  # noqa: F401
+from .attention_bwd import (  # noqa: F401
+    attention_bwd,
+    attention_bwd_keys,
+    attention_bwd_rows,
+    probabilities,
+)

@@ -28,7 +28,7 @@ import numpy as np
 
 from .attention import visible_mask
 
-__all__ = ["attention_bwd", "probabilities"]
+__all__ = ["attention_bwd", "attention_bwd_rows", "attention_bwd_keys", "probabilities"]
 
 
 def probabilities(q_rows, k, rows, causal: bool, window: int, scale: float):
@@ -83,3 +83,61 @@ def attention_bwd(q, k, v, do, causal: bool = False, window: int = -1,
                 dk[b, g] += scale * (ds.T @ q[b, h, rows])
                 dv[b, g] += p.T @ do[b, h, rows]
     return dq, dk, dv
+
+
+def _row_terms(q_rows, k, v, do_rows, rows, causal, window, scale):
+    """P and dS of the given query rows of one head, over all n keys."""
+    p = probabilities(q_rows, k, rows, causal, window, scale)
+    o = p @ v
+    dp = do_rows @ v.T
+    dsum = np.sum(do_rows * o, axis=1)
+    return p, p * (dp - dsum[:, None])
+
+
+def attention_bwd_rows(q, k, v, do, rows, causal: bool = False, window: int = -1,
+                       scale: float | None = None):
+    """dq of the query rows ``rows`` of one batch element, in float64.
+
+    q, do: [H, n, d]; k, v: [Hkv, n, d].  Returns dq [H, len(rows), d].
+    Same definitions as ``attention_bwd``, evaluated only on those rows.
+    """
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    H, n, d = q.shape
+    group = H // k.shape[0]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.zeros((H, rows.size, d))
+    for h in range(H):
+        g = h // group
+        _, ds = _row_terms(q[h, rows], k[g], v[g], do[h, rows], rows, causal, window, scale)
+        out[h] = scale * (ds @ k[g])
+    return out
+
+
+def attention_bwd_keys(q, k, v, do, keys, rows, causal: bool = False, window: int = -1,
+                       scale: float | None = None):
+    """dk, dv of the keys ``keys`` of one batch element, in float64.
+
+    q, do: [H, n, d]; k, v: [Hkv, n, d].  ``rows`` are the query rows summed
+    over; they must include every row that sees one of ``keys`` (rows that see
+    none add exactly zero).  Returns (dk, dv), each [Hkv, len(keys), d],
+    summed over the query heads of each key/value head.
+    """
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    H, n, d = q.shape
+    Hkv = k.shape[0]
+    group = H // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    keys = np.asarray(keys, dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64)
+    dk = np.zeros((Hkv, keys.size, d))
+    dv = np.zeros((Hkv, keys.size, d))
+    for h in range(H):
+        g = h // group
+        p, ds = _row_terms(q[h, rows], k[g], v[g], do[h, rows], rows, causal, window, scale)
+        dk[g] += scale * (ds[:, keys].T @ q[h, rows])
+        dv[g] += p[:, keys].T @ do[h, rows]
+    return dk, dv
+

@@ -14,6 +14,12 @@ import numpy as np
 #   log-sum-exp (both):              max |d lse| <= 1e-3
 TOL_BF16 = {"max_abs": 2e-2, "mean_abs": 2e-3, "lse": 1e-3}
 TOL_F32 = {"max_abs": 1e-4, "mean_abs": 1e-4, "lse": 1e-3}
+# Backward, per gradient tensor against the fp64 oracle: elementwise
+# |d| <= 2^-7 M + 1e-6 with M the rounding bound of tests/bwd_bounds.py, and
+# ||d||_F / ||ref||_F <= 8e-3 (about 2u, u = 2^-8 the bf16 unit roundoff) on
+# whole gradients;
+# a gradient that is zero by the mathematics: max |d| <= 1e-4.
+TOL_BWD = {"rel_fro": 8e-3, "zero_abs": 1e-4, "abs_floor": 1e-6}
 
 
 def say(*a):
@@ -67,3 +73,41 @@ def compare(o, lse, o_ref, lse_ref, tol, label):
     assert d.max() <= tol["max_abs"], f"{label}: max |dO| {d.max()}"
     assert d.mean() <= tol["mean_abs"], f"{label}: mean |dO| {d.mean()}"
     assert dl.max() <= tol["lse"], f"{label}: max |dlse| {dl.max()}"
+
+
+def rows_seeing(keys, n, causal, window):
+    """A contiguous range of query rows containing every row that sees one of
+    ``keys`` (causal: rows at or after the key, at most ``window`` later;
+    band: rows within ``window`` on either side; full: all rows)."""
+    keys = np.asarray(keys)
+    lo = keys.min() if causal else (keys.min() - window if window >= 0 else 0)
+    hi = keys.max() + window if window >= 0 else n - 1
+    return np.arange(max(int(lo), 0), min(int(hi), n - 1) + 1)
+
+
+def compare_grad(got, ref, bound, label, tol=TOL_BWD):
+    """Check one gradient tensor against the oracle's, with its bound M."""
+    from tests.bwd_bounds import BOUND_FACTOR
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape == bound.shape, f"{label}: shapes {got.shape} {ref.shape}"
+    assert np.isfinite(got).all(), f"{label}: non-finite gradient"
+    diff = np.abs(got - ref)
+    ratio = diff / (BOUND_FACTOR * bound + tol["abs_floor"])
+    rel_fro = np.linalg.norm(diff) / max(np.linalg.norm(ref), 1e-300)
+    worst = np.unravel_index(int(ratio.argmax()), ratio.shape)
+    say(f"  {label}: relF={rel_fro:.3e} max|d|={diff.max():.3e} "
+        f"max |d|/(2^-7 M)={ratio.max():.3f} at {tuple(int(x) for x in worst)} "
+        f"(max|ref|={np.abs(ref).max():.3e})")
+    if np.abs(ref).max() < 1e-9:
+        # Analytically zero gradient (every row sees only itself): what is left
+        # is fp32 summation-order noise in dP - D, far below any bf16 rounding.
+        assert diff.max() <= tol["zero_abs"], f"{label}: expected zeros, max |d| {diff.max()}"
+        return
+    assert ratio.max() <= 1.0, f"{label}: error above the rounding bound at {worst}"
+    # The Frobenius criterion is statistical (random rounding signs): it is
+    # applied to whole gradients, not to a handful of sampled rows, where one
+    # row with cancellation dominates it.
+    if got.size // got.shape[-1] >= 256:
+        assert rel_fro <= tol["rel_fro"], f"{label}: relative Frobenius error {rel_fro}"
+

@@ -31,7 +31,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"fa_fwd", "fa_decode", "fa_decode_workspace_bytes",
-                          "fa_strerror", "fa_version"}
+                          "fa_bwd", "fa_bwd_workspace_bytes", "fa_strerror", "fa_version"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -99,3 +99,37 @@ def test_workspace_size(lib):
     assert fa.fa_decode_workspace_bytes(64, 32, 65536, 128) >= big
     ws = fa.fa_decode_workspace_bytes(2, 8, 64, 128)
     assert _dec(wsb=ws - 1) == -4
+
+
+def _bwd(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+                B=1, H=2, Hkv=1, n=16, d=128, causal=0, window=-1, scale=0.1, dtype=0,
+                ws=FAKE, wsb=1 << 20)
+    args.update(kw)
+    return fa.lib().fa_bwd(args["q"], args["k"], args["v"], args["o"], args["lse"], args["do"],
+                           args["dq"], args["dk"], args["dv"], args["B"], args["H"],
+                           args["Hkv"], args["n"], args["d"], args["causal"], args["window"],
+                           ctypes.c_float(args["scale"]), args["dtype"], args["ws"],
+                           args["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(o=None), -1),
+    (dict(lse=None), -1), (dict(do=None), -1), (dict(dq=None), -1), (dict(dk=None), -1),
+    (dict(dv=None), -1),
+    (dict(B=0), -2), (dict(H=0), -2), (dict(Hkv=0), -2), (dict(n=0), -2), (dict(d=0), -2),
+    (dict(H=3, Hkv=2), -2), (dict(causal=2), -2), (dict(scale=0.0), -2),
+    (dict(scale=float("nan")), -2), (dict(n=1 << 25, d=128), -2),
+    (dict(d=96), -3), (dict(dtype=1), -3), (dict(dtype=7), -3),
+    (dict(ws=None), -4), (dict(wsb=1 * 2 * 16 * 4 - 1), -4),
+])
+def test_bwd_rejects(lib, kw, status):
+    assert _bwd(**kw) == status
+
+
+def test_bwd_workspace_size(lib):
+    # one float (D_i = <dO_i, O_i>) per query row
+    assert fa.fa_bwd_workspace_bytes(2, 8, 100, 128) == 2 * 8 * 100 * 4
+    assert fa.fa_bwd_workspace_bytes(0, 8, 100, 128) == 0
+    assert fa.fa_bwd_workspace_bytes(1, 1, 1 << 25, 128) == 0
+

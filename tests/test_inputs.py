@@ -4,7 +4,8 @@ import numpy as np
 import torch
 
 from io_aware_exact_fa_amd.inputs import (bf16_round, decode_inputs,
-                                          decode_lengths_and_table, prefill_inputs)
+                                          decode_lengths_and_table, grad_output,
+                                          prefill_inputs)
 
 
 def test_bf16_round_matches_torch_rne():
@@ -28,6 +29,17 @@ def test_prefill_deterministic_and_scaled():
     assert np.array_equal(half["q"], a["q"] * np.float32(0.5))
     f = prefill_inputs(1, 1, 1, 5, 4, seed=1, dtype="f32")
     assert f["q"].dtype == np.float32 and "q_bits" not in f
+
+
+def test_grad_output_independent_of_qkv():
+    a, abits = grad_output(1, 2, 33, 8, seed=4)
+    b, bbits = grad_output(1, 2, 33, 8, seed=4)
+    assert np.array_equal(abits, bbits) and a.shape == (1, 2, 33, 8)
+    assert np.array_equal(bf16_round(a)[1], abits)  # bf16-exact values
+    qkv = prefill_inputs(1, 2, 2, 33, 8, seed=4)
+    assert not np.array_equal(a, qkv["q"])  # its own stream, not a copy of Q
+    h, _ = grad_output(1, 2, 33, 8, seed=4, draw_scale=0.5)
+    assert np.array_equal(h, a * np.float32(0.5))
 
 
 def test_decode_table_is_a_permutation():

@@ -12,7 +12,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attention_bwd, attention_fwd
+from oracle import attention_bwd, attention_bwd_keys, attention_bwd_rows, attention_fwd
+from tests.gpu_util import rows_seeing
 
 MODES = [(False, -1), (True, -1), (False, 0), (False, 1), (False, 3), (True, 0), (True, 2)]
 
@@ -134,3 +135,28 @@ def test_linear_in_do_and_chunking():
     c = attention_bwd(q, k, v, 2 * d1 - 3 * d2, True, 7, 0.5, chunk=4)
     for x, y, z in zip(a, b, c):
         np.testing.assert_allclose(z, 2 * x - 3 * y, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal,window", MODES + [(False, 20), (True, 20)])
+def test_subset_functions_equal_full(causal, window):
+    """Row and key subsets give the full computation's values on those rows/keys,
+    also when the summed rows are cut down to the ones that see the keys."""
+    rng = np.random.default_rng(46)
+    H, Hkv, n, d = 4, 2, 41, 8
+    q, do = _rand(rng, 1, H, n, d), _rand(rng, 1, H, n, d)
+    k, v = _rand(rng, 1, Hkv, n, d), _rand(rng, 1, Hkv, n, d)
+    dq, dk, dv = attention_bwd(q, k, v, do, causal, window, 0.35)
+    rows = np.array([0, 1, 5, 17, 39, 40])
+    np.testing.assert_allclose(attention_bwd_rows(q[0], k[0], v[0], do[0], rows, causal,
+                                                  window, 0.35), dq[0][:, rows],
+                               rtol=0, atol=1e-13)
+    keys = np.array([0, 3, 20, 38, 40])
+    a_dk, a_dv = attention_bwd_keys(q[0], k[0], v[0], do[0], keys, np.arange(n), causal,
+                                    window, 0.35)
+    np.testing.assert_allclose(a_dk, dk[0][:, keys], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(a_dv, dv[0][:, keys], rtol=0, atol=1e-13)
+    seeing = rows_seeing(keys, n, causal, window)
+    b_dk, b_dv = attention_bwd_keys(q[0], k[0], v[0], do[0], keys, seeing, causal, window, 0.35)
+    np.testing.assert_allclose(b_dk, a_dk, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(b_dv, a_dv, rtol=0, atol=1e-13)
+
