@@ -1,7 +1,7 @@
 """Benchmark of the attention forward hot path on one MI355X.
 
-One step = one pass over both halves of the path on one batch of synthetic
-input already resident in HBM:
+One step = one pass over both halves of the forward path on one batch of
+synthetic input already resident in HBM:
   * prefill: causal self-attention with grouped-query heads, B=1, H=32,
     Hkv=8, n=65536, d=128, bf16 (draws x0.5), fp32 lse;
   * decode: paged flash-decoding, 64 sequences, 32 query / 8 KV heads, d=128,
@@ -14,8 +14,10 @@ average duration from HIP events on the stream it runs on.  The decode's KV
 GB/s (bytes of K and V that the sequences' lengths make visible, divided by
 split+merge duration) is reported beside it.  ``cpu_baseline`` times the fp64
 oracle on a bounded sample of the same prefill workload on the host cores.
+``backward`` times fa_bwd (the gradients) on the same prefill workload after
+the timed steps, outside the step.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--bwd-steps N]
 """
 
 from __future__ import annotations
@@ -78,6 +80,8 @@ def measured_traffic(kernel_key: str, src_hash: str):
 KERNEL_KEYS = {  # traffic.json key -> (kernel-name fragments, sources)
     "prefill_bf16": (("prefill_bf16_kernel<128",), ("prefill_bf16.hip", "common.hpp")),
     "decode": (("decode_split_kernel<128, 4>", "decode_combine_kernel"), ("decode.hip", "common.hpp")),
+    "backward": (("bwd_delta_kernel<128>", "bwd_dkdv_kernel<128>", "bwd_dq_kernel<128>"),
+                 ("backward.hip", "common.hpp")),
 }
 CALIBRATION_COPY_BYTES = 256 << 20
 
@@ -206,6 +210,56 @@ def time_other_workloads(fa, torch, np, bf, stream, reps: int = 20):
     return res
 
 
+def time_backward(fa, torch, bf, stream, q, k, v, o, lse, scale, steps: int):
+    """fa_bwd on the prefill workload (o, lse from its forward), HIP events.
+
+    Useful FLOPs: 10*d per visible pair (the five products of the chain rule:
+    S = Q K^T recomputed, dP = dO V^T, dV = P^T dO, dQ = dS K, dK = dS^T Q).
+    """
+    from io_aware_exact_fa_amd.inputs import grad_output
+    P = PREFILL
+    B, H, Hkv, n, d = P["B"], P["H"], P["Hkv"], P["n"], P["d"]
+    log("generating the output gradient")
+    _, do_bits = grad_output(B, H, n, d, seed=P["seed"], draw_scale=P["draw_scale"])
+    dout = bf(do_bits)
+    del do_bits
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq, dk, dv = (torch.empty((B, h, n, d), **f32) for h in (H, Hkv, Hkv))
+    ws_bytes = fa.fa_bwd_workspace_bytes(B, H, n, d)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+
+    def bwd():
+        fa.fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, n, d, P["causal"], P["window"],
+                  scale, fa.FA_BF16, ws, ws_bytes, stream)
+
+    bwd()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        bwd()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    pairs = inband_pairs(n, bool(P["causal"]), P["window"]) * B * H
+    flops = 10 * d * pairs
+    tf = flops / (ms * 1e-3) / 1e12
+    log(f"backward {ms:.3f} ms  {tf:.1f} TFLOP/s (10*d per in-band pair)")
+    traffic = measured_traffic("backward", source_hash("backward.hip", "common.hpp"))
+    del dout, dq, dk, dv, ws
+    return {
+        "workload": "backward of the prefill workload (same q, k, v; o and lse from fa_fwd; "
+                    "dO drawn like q)",
+        "value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4), "steps": steps,
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic,
+                     "kernel": "one fa_bwd call: bwd_delta + bwd_dkdv + bwd_dq kernels",
+                     "algorithmic_flops_per_launch": flops},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -216,6 +270,8 @@ def main():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc runs and exit "
                          "(no GPU needed)")
+    ap.add_argument("--bwd-steps", type=int, default=5,
+                    help="timed fa_bwd calls on the prefill workload (0: skip the backward)")
     ap.add_argument("--all-workloads", action="store_true",
                     help="also time every workload (fp32 n=256, causal n=4096, band n=32768) "
                          "and print one line each to stderr")
@@ -357,7 +413,11 @@ def main():
                          "kernel": "decode_split_kernel + decode_combine_kernel"},
         },
     }
-    del q, k, v, o, dq, dk, dv
+    del dq, dk, dv
+    if args.bwd_steps > 0:
+        out["backward"] = time_backward(fa, torch, bf, stream, q, k, v, o, lse, scale,
+                                        args.bwd_steps)
+    del q, k, v, o
     torch.cuda.empty_cache()
     if args.all_workloads:
         out["other_workloads"] = time_other_workloads(fa, torch, np, bf, stream)

@@ -14,7 +14,8 @@
 //   * bwd_delta_kernel: D_i = <dO_i, O_i> in fp32.
 //   * bwd_dkdv_kernel: a workgroup owns 128 keys of one (b, KV head); wave w
 //     owns 32 of them with K and V held in registers as MFMA B operands.  It
-//     streams (query head, 32-query tile) pairs through double-buffered LDS:
+//     streams (32-query tile, query head) pairs, top tile first, through
+//     double-buffered LDS:
 //     S = Q K^T and dP = dO V^T (v_mfma_f32_32x32x16_bf16; in the accumulator
 //     lane l owns key l%32 and 16 query rows), P and dS elementwise, then
 //     dV += P^T dO and dK += dS^T Q with P^T / dS^T taken straight from those
@@ -153,8 +154,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = a.n, G = a.H / a.Hkv;
   const int nkb = (n + BK - 1) / BK;
-  const int kblk = blockIdx.x % nkb;
-  const int bg = blockIdx.x / nkb;
+  // Rounds of B*Hkv workgroups, one key block each (heaviest causal blocks,
+  // the first ones, first); inside a round, groups are spread so that each
+  // XCD keeps the same (b, g) from round to round.
+  const int BG = a.B * a.Hkv;
+  const int kblk = blockIdx.x / BG;
+  const int p = blockIdx.x - kblk * BG;
+  const int bg = (BG & 7) == 0 ? (p & 7) * (BG >> 3) + (p >> 3) : p;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int causal = a.causal, window = a.window;
   auto lo_of = [&](int i) { return window >= 0 ? i - window : 0; };
@@ -203,8 +209,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     const int c = (s % CPR) ^ bswz<D>(r);
     st_off[j] = (unsigned)(r * RB + c * 16);
   }
-  auto head_of = [&](int t) { return g * G + t / nqt; };
-  auto qtile_of = [&](int t) { return qt_lo + t % nqt; };
+  // Query tiles are walked from the last one down, the group's heads
+  // innermost: the workgroups of one (b, g) that an XCD runs together start
+  // on the same tiles, and a replacement workgroup starts where the others
+  // started shortly before, so Q and dO tiles are mostly read from L2 (a key
+  // block further down simply stops earlier).
+  auto head_of = [&](int t) { return g * G + t % G; };
+  auto qtile_of = [&](int t) { return qt_hi - t / G; };
   auto stage = [&](int t, char* tq, char* to, float* tl, float* td) {
     const int h = head_of(t), q0 = qtile_of(t) * BQ;
     const size_t row0 = (size_t)(b * a.H + h) * n + q0;
@@ -335,8 +346,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = a.n;
   const int nqb = (n + BR - 1) / BR;
-  const int qblk = nqb - 1 - (int)(blockIdx.x % nqb);  // heaviest causal blocks first
-  const int bh = blockIdx.x / nqb;
+  // Rounds of B*H workgroups, one query block each (heaviest causal blocks
+  // first); inside a round, consecutive heads (those sharing a key/value head)
+  // go to the same XCD (workgroups are dealt round-robin over 8 XCDs), so
+  // their K/V reads share that XCD's L2.
+  const int BH = a.B * a.H;
+  const int round = blockIdx.x / BH;
+  const int p = blockIdx.x - round * BH;
+  const int qblk = a.causal ? nqb - 1 - round : round;
+  const int bh = (BH & 7) == 0 ? (p & 7) * (BH >> 3) + (p >> 3) : p;
   const int b = bh / a.H, h = bh % a.H;
   const int g = h / (a.H / a.Hkv);
   const int causal = a.causal, window = a.window;
