@@ -36,3 +36,4 @@ from .attention_bwd import (  # noqa: F401
     attention_bwd_rows,
     probabilities,
 )
+from .varlen import attention_paged_prefill, attention_varlen  # noqa: F401
