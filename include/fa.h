@@ -2,7 +2,7 @@
  * fa.h -- C ABI of libfa.so: exact attention (forward, decode, backward) for
  * AMD MI355X (gfx950).
  *
- * Three operations, all exact (no approximation of the softmax):
+ * All operations are exact (no approximation of the softmax):
  *
  *   fa_fwd     prefill / self-attention forward over a whole sequence, computed
  *              tile by tile with an online softmax so the n x n score matrix
@@ -13,6 +13,8 @@
  *              log-sum-exp weights.
  *   fa_bwd     gradients dq, dk, dv of fa_fwd's output, recomputing the
  *              probabilities tile by tile from the saved log-sum-exp.
+ *   fa_fwd_varlen  fa_fwd over a ragged batch packed without padding.
+ *   fa_fwd_paged   chunked prefill: new query chunks over paged KV histories.
  *
  * Sources (web pages on IO-aware exact attention):
  *   - charles2530 blog "算子与编译器：FlashAttention 与长上下文": §1 (the
@@ -93,6 +95,73 @@ typedef enum {
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int Hkv, int n, int d, int causal, int window,
            float scale, int dtype, void* stream);
+
+/*
+ * fa_fwd_varlen -- attention forward over a ragged batch (sequences of
+ * different lengths packed without padding).
+ *
+ * In batched prefill the requests differ in length and share one window; each
+ * request's traversal is clipped to its own length instead of computing over
+ * padding (xxqk.cn sliding-window prefill article §8.1).  Every sequence is an
+ * independent fa_fwd problem, positions counted from its first token.
+ *
+ *   q, o       [H,   total, d]  bf16 (o written): the packed tokens of all
+ *   k, v       [Hkv, total, d]  bf16               sequences, per head
+ *   lse        [H,   total]     float32, written (as fa_fwd)
+ *   cu_seqlens [B + 1] int32, DEVICE: sequence b owns rows
+ *              cu_seqlens[b] .. cu_seqlens[b+1]-1; cu_seqlens[0] = 0,
+ *              non-decreasing, cu_seqlens[B] = total, every length at most
+ *              max_seqlen.  Empty sequences are allowed.
+ *
+ * causal, window, scale as in fa_fwd.  Device-side guards: offsets are
+ * clamped into [0, total] and lengths into [0, max_seqlen]; they only keep
+ * memory accesses in bounds.
+ * Limits: B, H, Hkv, total, max_seqlen >= 1; H % Hkv == 0; d in {64, 128};
+ * dtype FA_BF16; H * total * d < 2^31.
+ * Errors: FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_LAUNCH.
+ */
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int32_t* cu_seqlens, int B, int H, int Hkv, int total,
+                  int max_seqlen, int d, int causal, int window, float scale,
+                  int dtype, void* stream);
+
+/*
+ * fa_fwd_paged -- chunked prefill over paged KV histories (prefix reuse).
+ *
+ * Requests that share or extend a long prefix should not redo its prefill:
+ * the cached keys and values are reused (charles2530 blog "算子与编译器：
+ * FlashAttention 与长上下文" §7), held in fixed-size pages (§5).  Each
+ * sequence brings a chunk of new queries whose keys and values the caller has
+ * already written into its pages; the chunk's queries are the LAST positions
+ * of the sequence and attend to its cached prefix and to the chunk itself.
+ *
+ *   q, o          [H, total_q, d] bf16 (o written), packed chunks
+ *   lse           [H, total_q] float32, written
+ *   kcache,vcache [num_pages, Hkv, page_size, d] bf16 (as fa_decode)
+ *   page_table    [B, max_pages] int32 (as fa_decode)
+ *   cu_seqlens_q  [B + 1] int32, DEVICE: chunk b owns rows
+ *                 cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (as fa_fwd_varlen,
+ *                 lengths at most max_seqlen_q)
+ *   seqlens_k     [B] int32, DEVICE: keys of sequence b, its chunk included
+ *                 (at least the chunk's length, at most max_pages*page_size)
+ *
+ * Query i of chunk b sits at position seqlens_k[b] - len_b + i; the keys it
+ * sees follow causal / window exactly as in fa_fwd at that position.  A
+ * one-query chunk is a decode step; a chunk with no prefix is fa_fwd_varlen.
+ * Device-side guards: offsets and lengths are clamped as in fa_fwd_varlen,
+ * seqlens_k into [0, max_pages*page_size]; a page id outside [0, num_pages)
+ * reads page 0; a query that sees no key (chunk longer than its keys) gives
+ * o = 0 and lse = -inf.  They only keep memory accesses in bounds.
+ * Limits: B, H, Hkv, total_q, max_seqlen_q, num_pages, max_pages >= 1;
+ * H % Hkv == 0; d in {64, 128}; page_size == 16; dtype FA_BF16.
+ * Errors: FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_LAUNCH.
+ */
+int fa_fwd_paged(const void* q, const void* kcache, const void* vcache,
+                 const int32_t* page_table, const int32_t* cu_seqlens_q,
+                 const int32_t* seqlens_k, void* o, float* lse, int B, int H, int Hkv,
+                 int d, int total_q, int max_seqlen_q, int num_pages, int page_size,
+                 int max_pages, int causal, int window, float scale, int dtype,
+                 void* stream);
 
 /*
  * fa_decode_workspace_bytes -- device workspace fa_decode needs for these

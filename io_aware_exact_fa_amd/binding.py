@@ -56,6 +56,12 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                          i32, i32, i32, f32, i32, vp, sz, vp]
     L.fa_bwd.restype = i32
+    L.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                i32, i32, f32, i32, vp]
+    L.fa_fwd_varlen.restype = i32
+    L.fa_fwd_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                               i32, i32, i32, i32, i32, i32, f32, i32, vp]
+    L.fa_fwd_paged.restype = i32
     L.fa_strerror.argtypes = [i32]
     L.fa_strerror.restype = ctypes.c_char_p
     L.fa_version.argtypes = []
@@ -97,6 +103,30 @@ def fa_fwd(q, k, v, o, lse, B, H, Hkv, n, d, causal, window, scale, dtype,
                       float(scale), int(dtype), _stream(stream))
     if st != 0:
         raise FaError(st, "fa_fwd")
+
+
+def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, H, Hkv, total, max_seqlen, d, causal,
+                  window, scale, dtype, stream=None) -> None:
+    """Raw C-ABI call; tensors or integer device addresses."""
+    st = lib().fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens),
+                             int(B), int(H), int(Hkv), int(total), int(max_seqlen), int(d),
+                             int(causal), int(window), float(scale), int(dtype),
+                             _stream(stream))
+    if st != 0:
+        raise FaError(st, "fa_fwd_varlen")
+
+
+def fa_fwd_paged(q, kcache, vcache, page_table, cu_seqlens_q, seqlens_k, o, lse, B, H, Hkv,
+                 d, total_q, max_seqlen_q, num_pages, page_size, max_pages, causal, window,
+                 scale, dtype, stream=None) -> None:
+    """Raw C-ABI call; tensors or integer device addresses."""
+    st = lib().fa_fwd_paged(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(page_table),
+                            _ptr(cu_seqlens_q), _ptr(seqlens_k), _ptr(o), _ptr(lse), int(B),
+                            int(H), int(Hkv), int(d), int(total_q), int(max_seqlen_q),
+                            int(num_pages), int(page_size), int(max_pages), int(causal),
+                            int(window), float(scale), int(dtype), _stream(stream))
+    if st != 0:
+        raise FaError(st, "fa_fwd_paged")
 
 
 def fa_decode_workspace_bytes(B, H, max_seqlen, d) -> int:
@@ -230,3 +260,52 @@ def flash_attn_bwd(q, k, v, o, lse, dout, causal: bool = False, window: int = -1
            int(window), scale, FA_BF16, workspace,
            workspace.numel() * workspace.element_size(), stream)
     return dq, dk, dv
+
+
+def flash_attn_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = False,
+                      window: int = -1, scale: float | None = None, stream=None):
+    """Ragged batch: q [H,total,d], k/v [Hkv,total,d] bf16; cu_seqlens [B+1] int32
+    (device) -> (o [H,total,d] bf16, lse [H,total] fp32)."""
+    import torch
+    _check_contig(q, k, v, cu_seqlens)
+    H, total, d = q.shape
+    Hkv = k.shape[0]
+    if q.dtype != torch.bfloat16 or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("fa_fwd_varlen takes bf16 q, k, v")
+    if tuple(k.shape) != (Hkv, total, d) or tuple(v.shape) != (Hkv, total, d):
+        raise ValueError("k and v must be [Hkv, total, d]")
+    if cu_seqlens.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
+    fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, cu_seqlens.numel() - 1, H, Hkv, total,
+                  max_seqlen, d, int(bool(causal)), int(window), scale, FA_BF16, stream)
+    return o, lse
+
+
+def flash_attn_paged(q, kcache, vcache, page_table, cu_seqlens_q, seqlens_k,
+                     max_seqlen_q: int, causal: bool = True, window: int = -1,
+                     scale: float | None = None, stream=None):
+    """Chunks over paged histories: q [H,total_q,d] bf16; caches [P,Hkv,16,d] bf16;
+    page_table [B,max_pages], cu_seqlens_q [B+1], seqlens_k [B] int32 (device)
+    -> (o [H,total_q,d] bf16, lse [H,total_q] fp32)."""
+    import torch
+    _check_contig(q, kcache, vcache, page_table, cu_seqlens_q, seqlens_k)
+    H, total_q, d = q.shape
+    P, Hkv, ps, d2 = kcache.shape
+    if d2 != d or tuple(vcache.shape) != tuple(kcache.shape):
+        raise ValueError("cache shapes disagree with q")
+    for t in (page_table, cu_seqlens_q, seqlens_k):
+        if t.dtype != torch.int32:
+            raise ValueError("page_table, cu_seqlens_q and seqlens_k must be int32")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    fa_fwd_paged(q, kcache, vcache, page_table, cu_seqlens_q, seqlens_k, o, lse,
+                 seqlens_k.numel(), H, Hkv, d, total_q, max_seqlen_q, P, ps,
+                 page_table.shape[1], int(bool(causal)), int(window), scale, FA_BF16, stream)
+    return o, lse
+

@@ -21,7 +21,7 @@ bool fits_i32(long long x) { return x >= 0 && x < (long long)INT_MAX; }
 
 extern "C" {
 
-int fa_version(void) { return (1 << 16) | 1; }
+int fa_version(void) { return (1 << 16) | 2; }
 
 const char* fa_strerror(int status) {
   switch (status) {
@@ -56,6 +56,57 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     e = fa::launch_prefill_f32(q, k, v, o, lse, B, H, Hkv, n, d, causal, window, scale, st);
   else
     return FA_ERR_UNSUPPORTED;
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int32_t* cu_seqlens, int B, int H, int Hkv, int total, int max_seqlen,
+                  int d, int causal, int window, float scale, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse || !cu_seqlens) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || Hkv < 1 || total < 1 || max_seqlen < 1 || d < 1) return FA_ERR_SHAPE;
+  if (H % Hkv != 0) return FA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
+  if (!scale_ok(scale)) return FA_ERR_SHAPE;
+  if (!fits_i32((long long)H * total * d) || !fits_i32((long long)B * H) ||
+      !fits_i32((long long)B + 1))
+    return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (max_seqlen > total) max_seqlen = total;
+  if (window < 0) window = -1;
+  if (window > max_seqlen) window = max_seqlen;
+  hipError_t e = fa::launch_prefill_bf16_varlen(q, k, v, o, lse, cu_seqlens, B, H, Hkv, total,
+                                                max_seqlen, d, causal, window, scale,
+                                                static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_fwd_paged(const void* q, const void* kcache, const void* vcache, const int32_t* page_table,
+                 const int32_t* cu_seqlens_q, const int32_t* seqlens_k, void* o, float* lse,
+                 int B, int H, int Hkv, int d, int total_q, int max_seqlen_q, int num_pages,
+                 int page_size, int max_pages, int causal, int window, float scale, int dtype,
+                 void* stream) {
+  if (!q || !kcache || !vcache || !page_table || !cu_seqlens_q || !seqlens_k || !o || !lse)
+    return FA_ERR_NULL;
+  if (B < 1 || H < 1 || Hkv < 1 || d < 1 || total_q < 1 || max_seqlen_q < 1 || num_pages < 1 ||
+      page_size < 1 || max_pages < 1)
+    return FA_ERR_SHAPE;
+  if (H % Hkv != 0) return FA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
+  if (!scale_ok(scale)) return FA_ERR_SHAPE;
+  if (!fits_i32((long long)H * total_q * d) || !fits_i32((long long)B * H) ||
+      !fits_i32((long long)B * max_pages) || !fits_i32((long long)max_pages * 16) ||
+      !fits_i32((long long)B + 1))
+    return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (page_size != 16 || dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (max_seqlen_q > total_q) max_seqlen_q = total_q;
+  if (window < 0) window = -1;
+  if (window > max_pages * 16) window = max_pages * 16;
+  hipError_t e = fa::launch_prefill_bf16_paged(q, kcache, vcache, page_table, cu_seqlens_q,
+                                               seqlens_k, o, lse, B, H, Hkv, d, total_q,
+                                               max_seqlen_q, num_pages, max_pages, causal,
+                                               window, scale, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

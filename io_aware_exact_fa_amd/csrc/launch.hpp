@@ -14,6 +14,20 @@ namespace fa {
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* o,
                                float* lse, int B, int H, int Hkv, int n, int d,
                                int causal, int window, float scale, hipStream_t stream);
+// Ragged batch: q, o [H, total, d]; k, v [Hkv, total, d]; lse [H, total];
+// cu_seqlens [B+1] device offsets.
+hipError_t launch_prefill_bf16_varlen(const void* q, const void* k, const void* v, void* o,
+                                      float* lse, const int* cu_seqlens, int B, int H, int Hkv,
+                                      int total, int max_seqlen, int d, int causal, int window,
+                                      float scale, hipStream_t stream);
+// Chunks over paged histories: q, o [H, total_q, d]; lse [H, total_q];
+// caches [num_pages, Hkv, 16, d]; page_table [B, max_pages].
+hipError_t launch_prefill_bf16_paged(const void* q, const void* kcache, const void* vcache,
+                                     const int* page_table, const int* cu_seqlens_q,
+                                     const int* seqlens_k, void* o, float* lse, int B, int H,
+                                     int Hkv, int d, int total_q, int max_seqlen_q, int num_pages,
+                                     int max_pages, int causal, int window, float scale,
+                                     hipStream_t stream);
 hipError_t launch_prefill_f32(const void* q, const void* k, const void* v, void* o,
                               float* lse, int B, int H, int Hkv, int n, int d,
                               int causal, int window, float scale, hipStream_t stream);

@@ -44,14 +44,36 @@
 
 namespace fa {
 
+// Layout of the sequences a launch covers.
+//   kDense : q, o [B, H, n, d]; k, v [B, Hkv, n, d]; lse [B, H, n].
+//   kVarlen: ragged batch packed per head: q, o [H, total, d]; k, v
+//            [Hkv, total, d]; lse [H, total]; sequence b owns rows
+//            cu_q[b] .. cu_q[b+1]-1 (xxqk.cn article §8.1: each request's
+//            traversal is clipped to its own length, no padding).
+//   kPaged : new chunks over paged histories (charles2530 blog §5, §7): q, o
+//            [H, total, d] packed like kVarlen; keys and values in pages
+//            [num_pages, Hkv, 16, d] behind page_table [B, max_pages];
+//            sequence b has seqlens_k[b] keys and its chunk's queries are the
+//            last positions among them.
+enum PrefillMode { kDense = 0, kVarlen = 1, kPaged = 2 };
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
 struct PrefillArgs {
   const __bf16* q;
-  const __bf16* k;
-  const __bf16* v;
+  const __bf16* k;  // kPaged: key pages
+  const __bf16* v;  // kPaged: value pages
   __bf16* o;
   float* lse;
   int B, H, Hkv, n, causal, window, nqb;
   float scale_log2;  // scale * log2(e)
+  // kVarlen / kPaged
+  const int* cu_q;        // [B+1] query (and, kVarlen, key) offsets
+  const int* seqlens_k;   // kPaged: [B] keys per sequence
+  const int* page_table;  // kPaged: [B, max_pages]
+  int total;              // packed rows per head
+  int max_seqlen;         // longest query run (grid size)
+  int max_pages, num_pages;
 };
 
 // LDS tiles are dense (no padding): row r of a tile holds D bf16 values as
@@ -65,6 +87,14 @@ __device__ __forceinline__ int swz(int row) {
     return ((row & 3) << 2) | ((row >> 2) & 3);
   else
     return row & 7;
+}
+
+// 16 bytes per lane from HBM straight into LDS through a 64-bit per-lane
+// address (paged tiles gather rows from several pages): lane i's bytes land at
+// lds + 16*i.
+__device__ __forceinline__ void global_load_lds16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
 // 16 bytes per lane from HBM straight into LDS: lane i's bytes land at
@@ -83,7 +113,7 @@ __device__ __forceinline__ void buffer_load_lds16(const void* base, int nbytes, 
 // probabilities stay <= 2^8 and most tiles skip the accumulator rescale.
 constexpr float kRescaleThreshold = 8.0f;
 
-template <int D, int NW, int BC>
+template <int D, int NW, int BC, int MODE>
 __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int BR = NW * 32;         // query rows per workgroup (32 per wave)
   constexpr int RB = D * 2;           // bytes per tile row
@@ -95,6 +125,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a)
   constexpr int NDB = D / 32;         // 32-wide head-dim blocks (PV output)
   constexpr int NKC = BC / 16;        // 16-key chunks (PV contraction)
   static_assert(BC * CPR % (64 * NW) == 0, "tile must split evenly over waves");
+  static_assert(MODE != kPaged || BC == 64, "a paged key tile is four 16-token pages");
 
   // Double-buffered K and V tiles (BC x D bf16 each).  Four separate objects,
   // so the compiler can tell the tile being read from the tile being filled
@@ -106,7 +137,6 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a)
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-  const int n = a.n;
   const int BH = a.B * a.H;
 
   // ---- workgroup -> (b, h, query tile) ----
@@ -118,29 +148,57 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a)
   if ((BH & 7) == 0) bh = (p & 7) * (BH >> 3) + (p >> 3);
   const int b = bh / a.H, h = bh - b * a.H;
   const int g = h / (a.H / a.Hkv);
-  const __bf16* Qh = a.q + (size_t)(b * a.H + h) * n * D;
-  const __bf16* Kh = a.k + (size_t)(b * a.Hkv + g) * n * D;
-  const __bf16* Vh = a.v + (size_t)(b * a.Hkv + g) * n * D;
-  __bf16* Oh = a.o + (size_t)(b * a.H + h) * n * D;
-  float* Lh = a.lse + (size_t)(b * a.H + h) * n;
+
+  // Rows of this (b, h): n_q queries, n_k keys, query i at position i + qoff
+  // among the keys.  Offsets read from memory are clamped so every access
+  // stays inside the buffers whatever they hold.
+  int n_q, n_k, qoff = 0;
+  const __bf16 *Qh, *Kh = nullptr, *Vh = nullptr;
+  __bf16* Oh;
+  float* Lh;
+  if constexpr (MODE == kDense) {
+    n_q = n_k = a.n;
+    Qh = a.q + (size_t)(b * a.H + h) * a.n * D;
+    Kh = a.k + (size_t)(b * a.Hkv + g) * a.n * D;
+    Vh = a.v + (size_t)(b * a.Hkv + g) * a.n * D;
+    Oh = a.o + (size_t)(b * a.H + h) * a.n * D;
+    Lh = a.lse + (size_t)(b * a.H + h) * a.n;
+  } else {
+    const int s0 = min(max(a.cu_q[b], 0), a.total);
+    n_q = min(max(a.cu_q[b + 1] - s0, 0), min(a.max_seqlen, a.total - s0));
+    Qh = a.q + ((size_t)h * a.total + s0) * D;
+    Oh = a.o + ((size_t)h * a.total + s0) * D;
+    Lh = a.lse + (size_t)h * a.total + s0;
+    if constexpr (MODE == kVarlen) {
+      n_k = n_q;
+      Kh = a.k + ((size_t)g * a.total + s0) * D;
+      Vh = a.v + ((size_t)g * a.total + s0) * D;
+    } else {
+      n_k = min(max(a.seqlens_k[b], 0), a.max_pages * 16);
+      qoff = n_k - n_q;
+    }
+  }
 
   const int causal = a.causal, window = a.window;
-  // Visible keys of row i form the interval [lo(i), hi(i)], both monotone in i.
-  auto lo_of = [&](int i) { return window >= 0 ? i - window : 0; };
+  // Visible keys of row i (at position i + qoff) form the interval
+  // [lo(i), hi(i)], both monotone in i.
+  auto lo_of = [&](int i) { return window >= 0 ? i + qoff - window : 0; };
   auto hi_of = [&](int i) {
-    int v = causal ? i : (window >= 0 ? i + window : n - 1);
-    return v < n - 1 ? v : n - 1;
+    int v = causal ? i + qoff : (window >= 0 ? i + qoff + window : n_k - 1);
+    return v < n_k - 1 ? v : n_k - 1;
   };
 
   const int q0 = qb * BR;
-  const int qlast = min(q0 + BR, n) - 1;
+  if (q0 >= n_q) return;  // past this sequence's rows (ragged batches)
+  const int qlast = min(q0 + BR, n_q) - 1;
   const int kt_lo = max(lo_of(q0), 0) / BC;
-  const int kt_hi = hi_of(qlast) / BC;
+  const int hi_last = hi_of(qlast);
+  const int kt_hi = hi_last < 0 ? -1 : hi_last / BC;
 
   // ---- this wave's 32 query rows; lane owns row wq0 + l32 ----
   const int wq0 = q0 + wave * 32;
-  const bool wave_rows = wq0 < n;
-  const int wr1 = min(wq0 + 32, n) - 1;
+  const bool wave_rows = wq0 < n_q;
+  const int wr1 = min(wq0 + 32, n_q) - 1;
   const int wlo0 = lo_of(wq0), whi0 = hi_of(wq0);
   const int wlo1 = lo_of(wr1), whi1 = hi_of(wr1);
   const int row = wq0 + l32;
@@ -150,8 +208,8 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a)
   bf16x8 qf[NDC];
 #pragma unroll
   for (int dc = 0; dc < NDC; ++dc)
-    qf[dc] = (row < n) ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)row * D + dc * 16 + hi * 8)
-                       : bf16x8{};
+    qf[dc] = (row < n_q) ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)row * D + dc * 16 + hi * 8)
+                         : bf16x8{};
 
   f32x16 acc[NDB];
 #pragma unroll
@@ -167,23 +225,59 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a)
   // end of the sequence read as zeros by the hardware range check (those keys
   // are masked and their zero values contribute nothing).
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  unsigned st_off[IPW];
+  unsigned st_off[IPW];  // byte offset of the slot's chunk in a dense tile
+  int st_row[IPW];       // tile row of the slot
 #pragma unroll
   for (int j = 0; j < IPW; ++j) {
     const int s = (wave_u * IPW + j) * 64 + lane;
     const int r = s / CPR;
     const int c = (s % CPR) ^ swz<D>(r);
     st_off[j] = (unsigned)(r * RB + c * 16);
+    st_row[j] = r;
   }
-  auto stage = [&](int kt, char* tk, char* tv) {
-    const int k0 = kt * BC;
-    const int bytes = (n - k0) * RB;
-    const __bf16* kb = Kh + (size_t)k0 * D;
-    const __bf16* vb = Vh + (size_t)k0 * D;
+  // Paged tiles: the four page ids of tile kt (pages past the sequence's
+  // last one repeat it; an id outside [0, num_pages) reads page 0 instead, so
+  // no access leaves the cache whatever the table holds).
+  const int* pt = nullptr;
+  if constexpr (MODE == kPaged) pt = a.page_table + (size_t)b * a.max_pages;
+  const int last_page = (n_k - 1) >> 4;
+  auto page_ids = [&](int kt) {
+    i32x4 id;
 #pragma unroll
-    for (int j = 0; j < IPW; ++j) {
-      buffer_load_lds16(kb, bytes, st_off[j], tk + (wave_u * IPW + j) * 1024);
-      buffer_load_lds16(vb, bytes, st_off[j], tv + (wave_u * IPW + j) * 1024);
+    for (int j = 0; j < 4; ++j) {
+      int x = pt[min(kt * 4 + j, last_page)];
+      x = (x < 0 || x >= a.num_pages) ? 0 : x;
+      id[j] = x;
+    }
+    return id;
+  };
+  auto stage = [&](int kt, char* tk, char* tv, i32x4 pid) {
+    const int k0 = kt * BC;
+    if constexpr (MODE != kPaged) {
+      (void)pid;
+      const int bytes = (n_k - k0) * RB;
+      const __bf16* kb = Kh + (size_t)k0 * D;
+      const __bf16* vb = Vh + (size_t)k0 * D;
+#pragma unroll
+      for (int j = 0; j < IPW; ++j) {
+        buffer_load_lds16(kb, bytes, st_off[j], tk + (wave_u * IPW + j) * 1024);
+        buffer_load_lds16(vb, bytes, st_off[j], tv + (wave_u * IPW + j) * 1024);
+      }
+    } else {
+      // Rows past the last key repeat the last key's row: finite values that
+      // the mask gives zero weight.
+#pragma unroll
+      for (int j = 0; j < IPW; ++j) {
+        const int re = min(k0 + st_row[j], n_k - 1) - k0;
+        const int pj = re >> 4;
+        const int pg = pj == 0 ? pid[0] : pj == 1 ? pid[1] : pj == 2 ? pid[2] : pid[3];
+        const size_t off = (((size_t)pg * a.Hkv + g) * 16 + (re & 15)) * RB +
+                           (st_off[j] - (unsigned)st_row[j] * RB);
+        global_load_lds16(reinterpret_cast<const char*>(a.k) + off,
+                          tk + (wave_u * IPW + j) * 1024);
+        global_load_lds16(reinterpret_cast<const char*>(a.v) + off,
+                          tv + (wave_u * IPW + j) * 1024);
+      }
     }
   };
 
@@ -297,17 +391,32 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a)
     }
   };
 
-  stage(kt_lo, sK0, sV0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  // Page ids are fetched one tile ahead of their stage (scalar loads).
+  i32x4 pid_next = i32x4{0, 0, 0, 0};
+  if (kt_lo <= kt_hi) {
+    if constexpr (MODE == kPaged) pid_next = page_ids(kt_lo);
+    stage(kt_lo, sK0, sV0, pid_next);
+    if constexpr (MODE == kPaged)
+      if (kt_lo + 1 <= kt_hi) pid_next = page_ids(kt_lo + 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
   // Unrolled by two so that each tile's buffer is a fixed LDS object.
   for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
-    if (kt + 1 <= kt_hi) stage(kt + 1, sK1, sV1);
+    if (kt + 1 <= kt_hi) {
+      stage(kt + 1, sK1, sV1, pid_next);
+      if constexpr (MODE == kPaged)
+        if (kt + 2 <= kt_hi) pid_next = page_ids(kt + 2);
+    }
     tile(kt, sK0, sV0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (kt + 1 > kt_hi) break;
-    if (kt + 2 <= kt_hi) stage(kt + 2, sK0, sV0);
+    if (kt + 2 <= kt_hi) {
+      stage(kt + 2, sK0, sV0, pid_next);
+      if constexpr (MODE == kPaged)
+        if (kt + 3 <= kt_hi) pid_next = page_ids(kt + 3);
+    }
     tile(kt + 1, sK1, sV1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -316,8 +425,10 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a)
   // ---- epilogue: O = acc / l, lse = ln(2) * (m + log2 l) ----
   if (!wave_rows) return;
   const float lt = sum_xor32(l_run);
-  if (row >= n) return;
-  const float inv = 1.f / lt;
+  if (row >= n_q) return;
+  // lt = 0 only for a row that sees no key (a chunk longer than its
+  // sequence's keys): o = 0, lse = -inf.
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
   __bf16* orow = Oh + (size_t)row * D;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -330,26 +441,25 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a)
     }
   if (hi == 0) {
     const float m_use = (m_ref == kNegInf) ? 0.f : m_ref;
-    Lh[row] = (m_use + log2_fast(lt)) * kLn2;
+    Lh[row] = lt > 0.f ? (m_use + log2_fast(lt)) * kLn2 : kNegInf;
   }
 }
 
-template <int D>
-static hipError_t launch_d(const PrefillArgs& a0, int B, int H, int n, hipStream_t stream) {
+template <int D, int MODE>
+static hipError_t launch_d(const PrefillArgs& a0, int rows, hipStream_t stream) {
   constexpr int NW = 4, BC = 64;
   constexpr int BR = NW * 32;
   PrefillArgs a = a0;
-  a.nqb = (n + BR - 1) / BR;
-  const long long grid = (long long)a.nqb * B * H;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, BC>), dim3((unsigned)grid), dim3(NW * 64), 0,
-                     stream, a);
+  a.nqb = (rows + BR - 1) / BR;
+  const long long grid = (long long)a.nqb * a.B * a.H;
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, BC, MODE>), dim3((unsigned)grid), dim3(NW * 64),
+                     0, stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                               int B, int H, int Hkv, int n, int d, int causal, int window,
-                               float scale, hipStream_t stream) {
-  PrefillArgs a;
+static PrefillArgs base_args(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int H, int Hkv, int causal, int window, float scale) {
+  PrefillArgs a{};
   a.q = static_cast<const __bf16*>(q);
   a.k = static_cast<const __bf16*>(k);
   a.v = static_cast<const __bf16*>(v);
@@ -358,13 +468,51 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void
   a.B = B;
   a.H = H;
   a.Hkv = Hkv;
-  a.n = n;
   a.causal = causal;
   a.window = window;
-  a.nqb = 0;
   a.scale_log2 = scale * kLog2e;
-  if (d == 128) return launch_d<128>(a, B, H, n, stream);
-  if (d == 64) return launch_d<64>(a, B, H, n, stream);
+  return a;
+}
+
+hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int B, int H, int Hkv, int n, int d, int causal, int window,
+                               float scale, hipStream_t stream) {
+  PrefillArgs a = base_args(q, k, v, o, lse, B, H, Hkv, causal, window, scale);
+  a.n = n;
+  if (d == 128) return launch_d<128, kDense>(a, n, stream);
+  if (d == 64) return launch_d<64, kDense>(a, n, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_bf16_varlen(const void* q, const void* k, const void* v, void* o,
+                                      float* lse, const int* cu_seqlens, int B, int H, int Hkv,
+                                      int total, int max_seqlen, int d, int causal, int window,
+                                      float scale, hipStream_t stream) {
+  PrefillArgs a = base_args(q, k, v, o, lse, B, H, Hkv, causal, window, scale);
+  a.cu_q = cu_seqlens;
+  a.total = total;
+  a.max_seqlen = max_seqlen;
+  if (d == 128) return launch_d<128, kVarlen>(a, max_seqlen, stream);
+  if (d == 64) return launch_d<64, kVarlen>(a, max_seqlen, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_bf16_paged(const void* q, const void* kcache, const void* vcache,
+                                     const int* page_table, const int* cu_seqlens_q,
+                                     const int* seqlens_k, void* o, float* lse, int B, int H,
+                                     int Hkv, int d, int total_q, int max_seqlen_q, int num_pages,
+                                     int max_pages, int causal, int window, float scale,
+                                     hipStream_t stream) {
+  PrefillArgs a = base_args(q, kcache, vcache, o, lse, B, H, Hkv, causal, window, scale);
+  a.cu_q = cu_seqlens_q;
+  a.seqlens_k = seqlens_k;
+  a.page_table = page_table;
+  a.total = total_q;
+  a.max_seqlen = max_seqlen_q;
+  a.num_pages = num_pages;
+  a.max_pages = max_pages;
+  if (d == 128) return launch_d<128, kPaged>(a, max_seqlen_q, stream);
+  if (d == 64) return launch_d<64, kPaged>(a, max_seqlen_q, stream);
   return hipErrorInvalidValue;
 }
 

@@ -13,6 +13,18 @@ Recipe (fixed so every consumer sees bit-identical inputs):
   * backward: the output gradient dO [B, H, n, d] is drawn from
     ``default_rng([seed, 3])`` (same draw_scale rule), so Q, K and V do not
     move when it is added;
+  * ragged batch: lengths from ``default_rng([seed, 4])`` (discrete uniform,
+    inclusive) unless given; then Q [H, T, d], K, V [Hkv, T, d] (T = sum of
+    lengths, sequences packed in order) drawn from ``default_rng(seed)`` in
+    that order;
+  * chunked prefill over pages: from ``default_rng([seed, 6])`` the cached
+    prefix lengths, the chunk lengths (both discrete uniform, inclusive) and a
+    permutation of the P = sum ceil((prefix + chunk) / page_size) physical
+    pages (sequence b takes its consecutive slice in logical order, as in
+    decode); the chunks' queries Q [H, total_q, d] from
+    ``default_rng([seed, 7])``; sequence b's K and V pages (prefix and chunk)
+    from ``default_rng([seed, 1, b])`` and ``default_rng([seed, 2, b])`` like
+    decode;
   * bf16 storage: round-to-nearest-even of the float32 draw to bfloat16;
     the returned float32 arrays hold exactly the rounded values;
   * decode: from ``default_rng(seed)``: the sequence lengths (discrete uniform
@@ -38,6 +50,8 @@ __all__ = [
     "bf16_bits_to_f32",
     "prefill_inputs",
     "grad_output",
+    "varlen_inputs",
+    "paged_prefill_inputs",
     "decode_lengths_and_table",
     "decode_sequence_kv",
     "decode_inputs",
@@ -100,6 +114,71 @@ def grad_output(B: int, H: int, n: int, d: int, seed: int,
     Returns (float32 values holding the bf16 numbers, raw uint16 bits).
     """
     return bf16_round(_draw(np.random.default_rng([seed, 3]), (B, H, n, d), draw_scale))
+
+
+def varlen_inputs(H: int, Hkv: int, d: int, seed: int, lengths=None, B: int = 0,
+                  min_len: int = 1, max_len: int = 1, draw_scale: float = 1.0) -> dict:
+    """Ragged batch packed per head: q [H, T, d], k, v [Hkv, T, d] (bf16-exact
+    float32 values and ``*_bits``), ``cu_seqlens`` [B+1] int32, ``lengths``."""
+    if lengths is None:
+        lengths = np.random.default_rng([seed, 4]).integers(min_len, max_len + 1, size=B)
+    lengths = np.asarray(lengths, dtype=np.int64)
+    T = int(lengths.sum())
+    rng = np.random.default_rng(seed)
+    out = {"lengths": lengths.astype(np.int32),
+           "cu_seqlens": np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)}
+    for name, heads in (("q", H), ("k", Hkv), ("v", Hkv)):
+        vals, bits = bf16_round(_draw(rng, (heads, T, d), draw_scale))
+        out[name] = vals
+        out[name + "_bits"] = bits
+    return out
+
+
+def paged_prefill_inputs(B: int, H: int, Hkv: int, d: int, page_size: int,
+                         prefix_min: int, prefix_max: int, chunk_min: int, chunk_max: int,
+                         seed: int, with_values: bool = True) -> dict:
+    """Chunks of new queries over paged histories (see the module recipe).
+
+    Returns seqlens_k [B] (prefix + chunk), chunk lengths, cu_seqlens_q [B+1],
+    q / q_bits [H, total_q, d], page_table [B, max_pages] (-1 where unused),
+    kcache_bits / vcache_bits [P, Hkv, page_size, d] (and float32 values when
+    ``with_values``), num_pages, max_pages.
+    """
+    rng = np.random.default_rng([seed, 6])
+    prefix = rng.integers(prefix_min, prefix_max + 1, size=B)
+    chunk = rng.integers(chunk_min, chunk_max + 1, size=B)
+    seqlens = (prefix + chunk).astype(np.int64)
+    pages = (seqlens + page_size - 1) // page_size
+    P = int(pages.sum())
+    perm = rng.permutation(P).astype(np.int32)
+    max_pages = int((prefix_max + chunk_max + page_size - 1) // page_size)
+    table = np.full((B, max(max_pages, 1)), -1, dtype=np.int32)
+    off = 0
+    for b in range(B):
+        table[b, :pages[b]] = perm[off:off + pages[b]]
+        off += int(pages[b])
+    cu_q = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+    q_vals, q_bits = bf16_round(_draw(np.random.default_rng([seed, 7]),
+                                      (H, int(cu_q[-1]), d), 1.0))
+    k_bits = np.empty((max(P, 1), Hkv, page_size, d), dtype=np.uint16)
+    v_bits = np.empty_like(k_bits)
+
+    def fill(b):
+        _, kb, _, vb = decode_sequence_kv(seed, b, int(pages[b]), Hkv, page_size, d)
+        phys = table[b, :pages[b]]
+        k_bits[phys] = kb
+        v_bits[phys] = vb
+
+    with ThreadPoolExecutor(max_workers=max(1, min(8, os.cpu_count() or 1))) as ex:
+        list(ex.map(fill, range(B)))
+    out = {"seqlens_k": seqlens.astype(np.int32), "chunk": chunk.astype(np.int32),
+           "prefix": prefix.astype(np.int32), "cu_seqlens_q": cu_q, "q": q_vals,
+           "q_bits": q_bits, "page_table": table, "num_pages": P, "max_pages": table.shape[1],
+           "page_size": page_size, "kcache_bits": k_bits, "vcache_bits": v_bits}
+    if with_values:
+        out["kcache"] = bf16_bits_to_f32(k_bits)
+        out["vcache"] = bf16_bits_to_f32(v_bits)
+    return out
 
 
 def decode_lengths_and_table(B: int, H: int, d: int, page_size: int,

@@ -31,7 +31,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"fa_fwd", "fa_decode", "fa_decode_workspace_bytes",
-                          "fa_bwd", "fa_bwd_workspace_bytes", "fa_strerror", "fa_version"}
+                          "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_varlen", "fa_fwd_paged",
+                          "fa_strerror", "fa_version"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -132,4 +133,50 @@ def test_bwd_workspace_size(lib):
     assert fa.fa_bwd_workspace_bytes(2, 8, 100, 128) == 2 * 8 * 100 * 4
     assert fa.fa_bwd_workspace_bytes(0, 8, 100, 128) == 0
     assert fa.fa_bwd_workspace_bytes(1, 1, 1 << 25, 128) == 0
+
+
+def _varlen(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, cu=FAKE, B=2, H=4, Hkv=2, total=100,
+                maxs=60, d=128, causal=1, window=-1, scale=0.1, dtype=0)
+    args.update(kw)
+    return fa.lib().fa_fwd_varlen(args["q"], args["k"], args["v"], args["o"], args["lse"],
+                                  args["cu"], args["B"], args["H"], args["Hkv"], args["total"],
+                                  args["maxs"], args["d"], args["causal"], args["window"],
+                                  ctypes.c_float(args["scale"]), args["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(o=None), -1),
+    (dict(lse=None), -1), (dict(cu=None), -1),
+    (dict(B=0), -2), (dict(H=0), -2), (dict(Hkv=0), -2), (dict(total=0), -2),
+    (dict(maxs=0), -2), (dict(d=0), -2), (dict(H=3, Hkv=2), -2), (dict(causal=3), -2),
+    (dict(scale=0.0), -2), (dict(total=1 << 24, H=8), -2),
+    (dict(d=96), -3), (dict(dtype=1), -3),
+])
+def test_varlen_rejects(lib, kw, status):
+    assert _varlen(**kw) == status
+
+
+def _paged_fwd(**kw):
+    args = dict(q=FAKE, kc=FAKE, vc=FAKE, pt=FAKE, cu=FAKE, sk=FAKE, o=FAKE, lse=FAKE, B=2,
+                H=8, Hkv=2, d=128, total=64, maxs=32, P=10, ps=16, maxp=4, causal=1,
+                window=-1, scale=0.1, dtype=0)
+    args.update(kw)
+    return fa.lib().fa_fwd_paged(args["q"], args["kc"], args["vc"], args["pt"], args["cu"],
+                                 args["sk"], args["o"], args["lse"], args["B"], args["H"],
+                                 args["Hkv"], args["d"], args["total"], args["maxs"], args["P"],
+                                 args["ps"], args["maxp"], args["causal"], args["window"],
+                                 ctypes.c_float(args["scale"]), args["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(kc=None), -1), (dict(vc=None), -1), (dict(pt=None), -1),
+    (dict(cu=None), -1), (dict(sk=None), -1), (dict(o=None), -1), (dict(lse=None), -1),
+    (dict(B=0), -2), (dict(H=0), -2), (dict(Hkv=0), -2), (dict(total=0), -2),
+    (dict(maxs=0), -2), (dict(P=0), -2), (dict(ps=0), -2), (dict(maxp=0), -2),
+    (dict(H=6, Hkv=4), -2), (dict(causal=-1), -2), (dict(scale=float("inf")), -2),
+    (dict(d=96), -3), (dict(ps=32), -3), (dict(dtype=1), -3),
+])
+def test_paged_fwd_rejects(lib, kw, status):
+    assert _paged_fwd(**kw) == status
 
