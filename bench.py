@@ -210,6 +210,78 @@ def time_other_workloads(fa, torch, np, bf, stream, reps: int = 20):
     return res
 
 
+VARLEN = dict(B=16, H=32, Hkv=8, d=128, min_len=1024, max_len=16384, seed=11)
+PAGED = dict(B=16, H=32, Hkv=8, d=128, prefix=(1024, 32768), chunk=(2048, 2048), seed=12)
+
+
+def _time(torch, stream, f, reps):
+    for _ in range(3):
+        f()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        f()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def time_ragged_workloads(fa, torch, np, bf, stream, reps: int = 20):
+    """Ragged-batch causal prefill and chunked prefill over paged histories."""
+    from io_aware_exact_fa_amd.inputs import paged_prefill_inputs, varlen_inputs
+
+    def i32(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(stream.device)
+
+    res = []
+    c = VARLEN
+    inp = varlen_inputs(c["H"], c["Hkv"], c["d"], seed=c["seed"], B=c["B"],
+                        min_len=c["min_len"], max_len=c["max_len"])
+    q, k, v = bf(inp["q_bits"]), bf(inp["k_bits"]), bf(inp["v_bits"])
+    cu = i32(inp["cu_seqlens"])
+    T, L = int(inp["cu_seqlens"][-1]), inp["lengths"].astype(np.int64)
+    o = torch.empty_like(q)
+    lse = torch.empty((c["H"], T), dtype=torch.float32, device=q.device)
+    ms = _time(torch, stream, lambda: fa.fa_fwd_varlen(
+        q, k, v, o, lse, cu, c["B"], c["H"], c["Hkv"], T, int(L.max()), c["d"], 1, -1,
+        1.0 / math.sqrt(c["d"]), fa.FA_BF16, stream), reps)
+    pairs = int((L * (L + 1) // 2).sum()) * c["H"]
+    tf = 4 * c["d"] * pairs / (ms * 1e-3) / 1e12
+    res.append({"workload": f"ragged causal prefill B{c['B']} H{c['H']}/Hkv{c['Hkv']} d{c['d']} "
+                            f"L~U[{c['min_len']},{c['max_len']}] (T={T})",
+                "ms": round(ms, 4), "TFLOP/s": round(tf, 2),
+                "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+    log(f"{res[-1]['workload']}: {ms:.4f} ms  {tf:.1f} TFLOP/s in-band")
+    del q, k, v, o, lse
+
+    c = PAGED
+    inp = paged_prefill_inputs(c["B"], c["H"], c["Hkv"], c["d"], 16, c["prefix"][0],
+                               c["prefix"][1], c["chunk"][0], c["chunk"][1], seed=c["seed"],
+                               with_values=False)
+    q, kc, vc = bf(inp["q_bits"]), bf(inp["kcache_bits"]), bf(inp["vcache_bits"])
+    pt, cuq, sk = i32(inp["page_table"]), i32(inp["cu_seqlens_q"]), i32(inp["seqlens_k"])
+    Tq = int(inp["cu_seqlens_q"][-1])
+    C, P = inp["chunk"].astype(np.int64), inp["prefix"].astype(np.int64)
+    o = torch.empty_like(q)
+    lse = torch.empty((c["H"], Tq), dtype=torch.float32, device=q.device)
+    ms = _time(torch, stream, lambda: fa.fa_fwd_paged(
+        q, kc, vc, pt, cuq, sk, o, lse, c["B"], c["H"], c["Hkv"], c["d"], Tq, int(C.max()),
+        kc.shape[0], 16, pt.shape[1], 1, -1, 1.0 / math.sqrt(c["d"]), fa.FA_BF16, stream), reps)
+    pairs = int((C * P + C * (C + 1) // 2).sum()) * c["H"]
+    tf = 4 * c["d"] * pairs / (ms * 1e-3) / 1e12
+    res.append({"workload": f"chunked causal prefill over 16-token pages B{c['B']} "
+                            f"H{c['H']}/Hkv{c['Hkv']} d{c['d']} prefix~U[{c['prefix'][0]},"
+                            f"{c['prefix'][1]}] chunk {c['chunk'][0]}",
+                "ms": round(ms, 4), "TFLOP/s": round(tf, 2),
+                "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+    log(f"{res[-1]['workload']}: {ms:.4f} ms  {tf:.1f} TFLOP/s in-band")
+    del q, kc, vc, o, lse
+    torch.cuda.empty_cache()
+    return res
+
+
 def time_backward(fa, torch, bf, stream, q, k, v, o, lse, scale, steps: int):
     """fa_bwd on the prefill workload (o, lse from its forward), HIP events.
 
@@ -273,8 +345,9 @@ def main():
     ap.add_argument("--bwd-steps", type=int, default=5,
                     help="timed fa_bwd calls on the prefill workload (0: skip the backward)")
     ap.add_argument("--all-workloads", action="store_true",
-                    help="also time every workload (fp32 n=256, causal n=4096, band n=32768) "
-                         "and print one line each to stderr")
+                    help="also time every workload (fp32 n=256, causal n=4096, band n=32768, "
+                         "ragged batch, chunked prefill over pages) and print one line each "
+                         "to stderr")
     args = ap.parse_args()
     if args.traffic_from:
         rec = traffic_from_counters(*args.traffic_from)
@@ -420,7 +493,8 @@ def main():
     del q, k, v, o
     torch.cuda.empty_cache()
     if args.all_workloads:
-        out["other_workloads"] = time_other_workloads(fa, torch, np, bf, stream)
+        out["other_workloads"] = (time_other_workloads(fa, torch, np, bf, stream) +
+                                  time_ragged_workloads(fa, torch, np, bf, stream))
     log("timing the oracle on a bounded sample")
     out["cpu_baseline"] = cpu_baseline(pin, max(1, args.cpu_rows),
                                        heads=[0, 5, 10, 15, 16, 21, 26, 31])

@@ -37,7 +37,9 @@
 //     chunk swizzle instead of padding.
 //   * Grid order: heaviest causal query tiles first; inside each round of B*H
 //     tiles, workgroups that share a key/value head are placed on the same XCD
-//     (dispatch is round-robin over the 8 XCDs), so their K/V reads share L2.
+//     (dispatch is round-robin over the 8 XCDs), so their K/V reads share L2,
+//     and the key/value groups are dealt to the XCDs in turn so every XCD gets
+//     an equal share of every sequence.
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -144,10 +146,26 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a)
   const int round = idx / BH;
   const int p = idx - round * BH;
   const int qb = a.causal ? (a.nqb - 1 - round) : round;
-  int bh = p;
-  if ((BH & 7) == 0) bh = (p & 7) * (BH >> 3) + (p >> 3);
-  const int b = bh / a.H, h = bh - b * a.H;
-  const int g = h / (a.H / a.Hkv);
+  // Inside a round, workgroup p runs on XCD p % 8 (round-robin dispatch).
+  // Key/value groups (b, g) are dealt to XCDs in turn and a group's G query
+  // heads follow each other on its XCD: they read the same K/V tiles from one
+  // L2, and every XCD gets an equal share of every sequence (ragged batches
+  // stay balanced).
+  const int G = a.H / a.Hkv;
+  int b, h, g;
+  if (((a.B * a.Hkv) & 7) == 0) {
+    const int j = p >> 3;
+    const int u = (p & 7) + 8 * (j / G);  // (b, g) unit
+    b = u / a.Hkv;
+    g = u - b * a.Hkv;
+    h = g * G + (j - (j / G) * G);
+  } else {
+    // fewer than 8 groups per XCD round: consecutive heads per XCD
+    const int bh = (BH & 7) == 0 ? (p & 7) * (BH >> 3) + (p >> 3) : p;
+    b = bh / a.H;
+    h = bh - b * a.H;
+    g = h / G;
+  }
 
   // Rows of this (b, h): n_q queries, n_k keys, query i at position i + qoff
   // among the keys.  Offsets read from memory are clamped so every access
