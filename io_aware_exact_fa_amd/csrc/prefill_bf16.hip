@@ -259,14 +259,12 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a)
   const int* pt = nullptr;
   if constexpr (MODE == kPaged) pt = a.page_table + (size_t)b * a.max_pages;
   const int last_page = (n_k - 1) >> 4;
+  // The loads are issued a tile ahead; the range check happens at the stage
+  // that uses them, so nothing waits for the loads until then.
   auto page_ids = [&](int kt) {
     i32x4 id;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int x = pt[min(kt * 4 + j, last_page)];
-      x = (x < 0 || x >= a.num_pages) ? 0 : x;
-      id[j] = x;
-    }
+    for (int j = 0; j < 4; ++j) id[j] = pt[min(kt * 4 + j, last_page)];
     return id;
   };
   auto stage = [&](int kt, char* tk, char* tv, i32x4 pid) {
@@ -288,7 +286,8 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a)
       for (int j = 0; j < IPW; ++j) {
         const int re = min(k0 + st_row[j], n_k - 1) - k0;
         const int pj = re >> 4;
-        const int pg = pj == 0 ? pid[0] : pj == 1 ? pid[1] : pj == 2 ? pid[2] : pid[3];
+        int pg = pj == 0 ? pid[0] : pj == 1 ? pid[1] : pj == 2 ? pid[2] : pid[3];
+        pg = (pg < 0 || pg >= a.num_pages) ? 0 : pg;
         const size_t off = (((size_t)pg * a.Hkv + g) * 16 + (re & 15)) * RB +
                            (st_off[j] - (unsigned)st_row[j] * RB);
         global_load_lds16(reinterpret_cast<const char*>(a.k) + off,
