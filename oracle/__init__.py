@@ -37,3 +37,4 @@ from .attention_bwd import (  # noqa: F401
     probabilities,
 )
 from .varlen import attention_paged_prefill, attention_varlen  # noqa: F401
+from .blocksparse import attention_block_sparse, attention_masked  # noqa: F401
