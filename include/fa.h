@@ -15,6 +15,7 @@
  *              probabilities tile by tile from the saved log-sum-exp.
  *   fa_fwd_varlen  fa_fwd over a ragged batch packed without padding.
  *   fa_fwd_paged   chunked prefill: new query chunks over paged KV histories.
+ *   fa_fwd_blocksparse  fa_fwd restricted to the kept blocks of a layout.
  *
  * Sources (web pages on IO-aware exact attention):
  *   - charles2530 blog "算子与编译器：FlashAttention 与长上下文": §1 (the
@@ -162,6 +163,31 @@ int fa_fwd_paged(const void* q, const void* kcache, const void* vcache,
                  int d, int total_q, int max_seqlen_q, int num_pages, int page_size,
                  int max_pages, int causal, int window, float scale, int dtype,
                  void* stream);
+
+/*
+ * fa_fwd_blocksparse -- attention forward with a block-sparse layout.
+ *
+ * Block-sparse FlashAttention ("FlashAttention 深度解析：大模型长序列的算力解放",
+ * ruiowl.com, §四) computes only the kept blocks of the score matrix; the
+ * sliding-window block skip (xxqk.cn article §5) is the band case.  The
+ * score matrix of each head is cut into blocks of block_q query rows by
+ * block_k keys; key j is visible to query i when layout[l, i / block_q,
+ * j / block_k] != 0 AND causal / window (as in fa_fwd) allow it.  Dropped
+ * blocks are never read.  A row with no visible key gets o = 0, lse = -inf.
+ *
+ *   q, k, v, o, lse  as fa_fwd (dense [B, heads, n, d] layout)
+ *   layout  uint8 [layout_heads, ceil(n/block_q), ceil(n/block_k)], DEVICE,
+ *           C order; layout_heads = 1 (one layout for every head) or H (one
+ *           per query head, l = h); shared by the whole batch.
+ *
+ * Limits: as fa_fwd, plus block_q == 128, block_k in {64, 128},
+ * layout_heads in {1, H}, n <= 131072; dtype FA_BF16.
+ * Errors: FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_LAUNCH.
+ */
+int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                       const uint8_t* layout, int layout_heads, int B, int H, int Hkv,
+                       int n, int d, int block_q, int block_k, int causal, int window,
+                       float scale, int dtype, void* stream);
 
 /*
  * fa_decode_workspace_bytes -- device workspace fa_decode needs for these

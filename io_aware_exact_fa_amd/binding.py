@@ -62,6 +62,9 @@ def lib() -> ctypes.CDLL:
     L.fa_fwd_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                i32, i32, i32, i32, i32, i32, f32, i32, vp]
     L.fa_fwd_paged.restype = i32
+    L.fa_fwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                     i32, i32, i32, i32, f32, i32, vp]
+    L.fa_fwd_blocksparse.restype = i32
     L.fa_strerror.argtypes = [i32]
     L.fa_strerror.restype = ctypes.c_char_p
     L.fa_version.argtypes = []
@@ -127,6 +130,17 @@ def fa_fwd_paged(q, kcache, vcache, page_table, cu_seqlens_q, seqlens_k, o, lse,
                             int(window), float(scale), int(dtype), _stream(stream))
     if st != 0:
         raise FaError(st, "fa_fwd_paged")
+
+
+def fa_fwd_blocksparse(q, k, v, o, lse, layout, layout_heads, B, H, Hkv, n, d, block_q,
+                       block_k, causal, window, scale, dtype, stream=None) -> None:
+    """Raw C-ABI call; tensors or integer device addresses."""
+    st = lib().fa_fwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(layout),
+                                  int(layout_heads), int(B), int(H), int(Hkv), int(n), int(d),
+                                  int(block_q), int(block_k), int(causal), int(window),
+                                  float(scale), int(dtype), _stream(stream))
+    if st != 0:
+        raise FaError(st, "fa_fwd_blocksparse")
 
 
 def fa_decode_workspace_bytes(B, H, max_seqlen, d) -> int:
@@ -307,5 +321,31 @@ def flash_attn_paged(q, kcache, vcache, page_table, cu_seqlens_q, seqlens_k,
     fa_fwd_paged(q, kcache, vcache, page_table, cu_seqlens_q, seqlens_k, o, lse,
                  seqlens_k.numel(), H, Hkv, d, total_q, max_seqlen_q, P, ps,
                  page_table.shape[1], int(bool(causal)), int(window), scale, FA_BF16, stream)
+    return o, lse
+
+
+def flash_attn_blocksparse(q, k, v, layout, block_q: int = 128, block_k: int = 64,
+                           causal: bool = False, window: int = -1,
+                           scale: float | None = None, stream=None):
+    """q [B,H,n,d], k/v [B,Hkv,n,d] bf16; layout uint8 [1 or H, ceil(n/block_q),
+    ceil(n/block_k)] (device) -> (o, lse) as flash_attn_fwd."""
+    import torch
+    _check_contig(q, k, v, layout)
+    B, H, n, d = q.shape
+    Hkv = k.shape[1]
+    if q.dtype != torch.bfloat16 or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("fa_fwd_blocksparse takes bf16 q, k, v")
+    if tuple(k.shape) != (B, Hkv, n, d) or tuple(v.shape) != (B, Hkv, n, d):
+        raise ValueError("k and v must be [B, Hkv, n, d]")
+    lh = layout.shape[0]
+    if layout.dtype != torch.uint8 or tuple(layout.shape[1:]) != (-(-n // block_q),
+                                                                    -(-n // block_k)):
+        raise ValueError("layout must be uint8 [1 or H, ceil(n/block_q), ceil(n/block_k)]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, n), dtype=torch.float32, device=q.device)
+    fa_fwd_blocksparse(q, k, v, o, lse, layout, lh, B, H, Hkv, n, d, block_q, block_k,
+                       int(bool(causal)), int(window), scale, FA_BF16, stream)
     return o, lse
 

@@ -21,7 +21,7 @@ bool fits_i32(long long x) { return x >= 0 && x < (long long)INT_MAX; }
 
 extern "C" {
 
-int fa_version(void) { return (1 << 16) | 2; }
+int fa_version(void) { return (1 << 16) | 3; }
 
 const char* fa_strerror(int status) {
   switch (status) {
@@ -78,6 +78,29 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
   hipError_t e = fa::launch_prefill_bf16_varlen(q, k, v, o, lse, cu_seqlens, B, H, Hkv, total,
                                                 max_seqlen, d, causal, window, scale,
                                                 static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                       const uint8_t* layout, int layout_heads, int B, int H, int Hkv, int n,
+                       int d, int block_q, int block_k, int causal, int window, float scale,
+                       int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse || !layout) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || Hkv < 1 || n < 1 || d < 1) return FA_ERR_SHAPE;
+  if (H % Hkv != 0) return FA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
+  if (!scale_ok(scale)) return FA_ERR_SHAPE;
+  if (layout_heads != 1 && layout_heads != H) return FA_ERR_SHAPE;
+  if (!fits_i32((long long)n * d) || !fits_i32((long long)B * H)) return FA_ERR_SHAPE;
+  if (n > 131072) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (block_q != 128 || (block_k != 64 && block_k != 128)) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (window < 0) window = -1;
+  if (window > n) window = n;
+  hipError_t e = fa::launch_prefill_bf16_blocksparse(q, k, v, o, lse, layout, layout_heads, B,
+                                                     H, Hkv, n, d, block_k, causal, window,
+                                                     scale, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -28,6 +28,12 @@ hipError_t launch_prefill_bf16_paged(const void* q, const void* kcache, const vo
                                      int Hkv, int d, int total_q, int max_seqlen_q, int num_pages,
                                      int max_pages, int causal, int window, float scale,
                                      hipStream_t stream);
+// Block-sparse: dense layout plus layout [layout_heads, ceil(n/128), ceil(n/block_k)].
+hipError_t launch_prefill_bf16_blocksparse(const void* q, const void* k, const void* v, void* o,
+                                           float* lse, const unsigned char* layout,
+                                           int layout_heads, int B, int H, int Hkv, int n, int d,
+                                           int block_k, int causal, int window, float scale,
+                                           hipStream_t stream);
 hipError_t launch_prefill_f32(const void* q, const void* k, const void* v, void* o,
                               float* lse, int B, int H, int Hkv, int n, int d,
                               int causal, int window, float scale, hipStream_t stream);

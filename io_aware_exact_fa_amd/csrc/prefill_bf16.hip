@@ -57,7 +57,16 @@ namespace fa {
 //            [num_pages, Hkv, 16, d] behind page_table [B, max_pages];
 //            sequence b has seqlens_k[b] keys and its chunk's queries are the
 //            last positions among them.
-enum PrefillMode { kDense = 0, kVarlen = 1, kPaged = 2 };
+//   kBlockSparse: the dense layout plus a 0/1 layout over blocks of 128 query
+//            rows by block_k keys ([layout_heads, ceil(n/128),
+//            ceil(n/block_k)], shared by the batch, one per head or one for
+//            all); a workgroup visits only its kept key tiles ("Block-Sparse
+//            FlashAttention", ruiowl.com deep-dive §四; the band skip of the
+//            xxqk.cn article §5 is the case of a band layout).
+enum PrefillMode { kDense = 0, kVarlen = 1, kPaged = 2, kBlockSparse = 3 };
+
+// Most key tiles a block-sparse workgroup can list (n <= 2048 * 64).
+constexpr int kMaxSparseTiles = 2048;
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
@@ -76,6 +85,9 @@ struct PrefillArgs {
   int total;              // packed rows per head
   int max_seqlen;         // longest query run (grid size)
   int max_pages, num_pages;
+  // kBlockSparse
+  const unsigned char* layout;
+  int layout_heads, layout_cols, tile_shift;  // tile_shift: log2(block_k / 64)
 };
 
 // LDS tiles are dense (no padding): row r of a tile holds D bf16 values as
@@ -174,14 +186,16 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a)
   const __bf16 *Qh, *Kh = nullptr, *Vh = nullptr;
   __bf16* Oh;
   float* Lh;
-  if constexpr (MODE == kDense) {
+  static_assert(MODE == kDense || MODE == kVarlen || MODE == kPaged || MODE == kBlockSparse,
+                "unknown layout mode");
+  if constexpr (MODE == kDense || MODE == kBlockSparse) {  // [B, heads, n, d]
     n_q = n_k = a.n;
     Qh = a.q + (size_t)(b * a.H + h) * a.n * D;
     Kh = a.k + (size_t)(b * a.Hkv + g) * a.n * D;
     Vh = a.v + (size_t)(b * a.Hkv + g) * a.n * D;
     Oh = a.o + (size_t)(b * a.H + h) * a.n * D;
     Lh = a.lse + (size_t)(b * a.H + h) * a.n;
-  } else {
+  } else {  // kVarlen, kPaged: packed rows located through cu_q
     const int s0 = min(max(a.cu_q[b], 0), a.total);
     n_q = min(max(a.cu_q[b + 1] - s0, 0), min(a.max_seqlen, a.total - s0));
     Qh = a.q + ((size_t)h * a.total + s0) * D;
@@ -408,33 +422,70 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a)
     }
   };
 
+  // The key tiles visited, in order: kt_lo .. kt_hi, or for a block-sparse
+  // workgroup the kept ones among them, listed in LDS by wave 0 (ballot +
+  // prefix count over 64 tiles at a time).
+  int nt = kt_hi - kt_lo + 1;
+  unsigned short* tiles = nullptr;
+  if constexpr (MODE == kBlockSparse) {
+    __shared__ unsigned short sTiles[kMaxSparseTiles];
+    __shared__ int sCount;
+    tiles = sTiles;
+    const int lh = a.layout_heads == 1 ? 0 : h;
+    const unsigned char* lay =
+        a.layout + ((size_t)lh * a.nqb + qb) * (size_t)a.layout_cols;
+    if (wave_u == 0) {
+      int cnt = 0;
+      for (int c0 = kt_lo; c0 <= kt_hi; c0 += 64) {
+        const int kt = c0 + lane;
+        // every lane reads an entry of its own row (index clamped to kt_hi)
+        const bool on = (lay[min(kt, kt_hi) >> a.tile_shift] != 0) && kt <= kt_hi;
+        const unsigned long long m = __builtin_amdgcn_ballot_w64(on);
+        const int before = __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((unsigned)m, 0));
+        if (on) sTiles[cnt + before] = (unsigned short)kt;
+        cnt += __builtin_popcountll(m);
+      }
+      if (lane == 0) sCount = cnt;
+    }
+    __syncthreads();
+    nt = __builtin_amdgcn_readfirstlane(sCount);
+  }
+  auto kt_at = [&](int i) {
+    if constexpr (MODE == kBlockSparse)
+      return (int)__builtin_amdgcn_readfirstlane(tiles[i]);
+    else
+      return kt_lo + i;
+  };
+
   // Page ids are fetched one tile ahead of their stage (scalar loads).
   i32x4 pid_next = i32x4{0, 0, 0, 0};
-  if (kt_lo <= kt_hi) {
+  if (nt > 0) {
     if constexpr (MODE == kPaged) pid_next = page_ids(kt_lo);
-    stage(kt_lo, sK0, sV0, pid_next);
+    stage(kt_at(0), sK0, sV0, pid_next);
     if constexpr (MODE == kPaged)
-      if (kt_lo + 1 <= kt_hi) pid_next = page_ids(kt_lo + 1);
+      if (1 < nt) pid_next = page_ids(kt_lo + 1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
   // Unrolled by two so that each tile's buffer is a fixed LDS object.
-  for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
-    if (kt + 1 <= kt_hi) {
-      stage(kt + 1, sK1, sV1, pid_next);
+  for (int i = 0; i < nt; i += 2) {
+    const int kt = kt_at(i);
+    if (i + 1 < nt) {
+      stage(kt_at(i + 1), sK1, sV1, pid_next);
       if constexpr (MODE == kPaged)
-        if (kt + 2 <= kt_hi) pid_next = page_ids(kt + 2);
+        if (i + 2 < nt) pid_next = page_ids(kt + 2);
     }
     tile(kt, sK0, sV0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (kt + 1 > kt_hi) break;
-    if (kt + 2 <= kt_hi) {
-      stage(kt + 2, sK0, sV0, pid_next);
+    if (i + 1 >= nt) break;
+    if (i + 2 < nt) {
+      stage(kt_at(i + 2), sK0, sV0, pid_next);
       if constexpr (MODE == kPaged)
-        if (kt + 3 <= kt_hi) pid_next = page_ids(kt + 3);
+        if (i + 3 < nt) pid_next = page_ids(kt + 3);
     }
-    tile(kt + 1, sK1, sV1);
+    tile(kt_at(i + 1), sK1, sV1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
@@ -511,6 +562,22 @@ hipError_t launch_prefill_bf16_varlen(const void* q, const void* k, const void* 
   a.max_seqlen = max_seqlen;
   if (d == 128) return launch_d<128, kVarlen>(a, max_seqlen, stream);
   if (d == 64) return launch_d<64, kVarlen>(a, max_seqlen, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_bf16_blocksparse(const void* q, const void* k, const void* v, void* o,
+                                           float* lse, const unsigned char* layout,
+                                           int layout_heads, int B, int H, int Hkv, int n, int d,
+                                           int block_k, int causal, int window, float scale,
+                                           hipStream_t stream) {
+  PrefillArgs a = base_args(q, k, v, o, lse, B, H, Hkv, causal, window, scale);
+  a.n = n;
+  a.layout = layout;
+  a.layout_heads = layout_heads;
+  a.layout_cols = (n + block_k - 1) / block_k;
+  a.tile_shift = block_k == 128 ? 1 : 0;
+  if (d == 128) return launch_d<128, kBlockSparse>(a, n, stream);
+  if (d == 64) return launch_d<64, kBlockSparse>(a, n, stream);
   return hipErrorInvalidValue;
 }
 

@@ -25,6 +25,11 @@ Recipe (fixed so every consumer sees bit-identical inputs):
     ``default_rng([seed, 7])``; sequence b's K and V pages (prefix and chunk)
     from ``default_rng([seed, 1, b])`` and ``default_rng([seed, 2, b])`` like
     decode;
+  * block-sparse layouts: [heads, nqb, nkb] uint8 from
+    ``default_rng([seed, 8])``: each block kept with probability ``density``,
+    plus (optionally) a local band of ``local`` key blocks on each side of the
+    diagonal (block indices scaled by block_q / block_k) and the first
+    ``global_cols`` key-block columns;
   * bf16 storage: round-to-nearest-even of the float32 draw to bfloat16;
     the returned float32 arrays hold exactly the rounded values;
   * decode: from ``default_rng(seed)``: the sequence lengths (discrete uniform
@@ -52,6 +57,7 @@ __all__ = [
     "grad_output",
     "varlen_inputs",
     "paged_prefill_inputs",
+    "block_layout",
     "decode_lengths_and_table",
     "decode_sequence_kv",
     "decode_inputs",
@@ -179,6 +185,21 @@ def paged_prefill_inputs(B: int, H: int, Hkv: int, d: int, page_size: int,
         out["kcache"] = bf16_bits_to_f32(k_bits)
         out["vcache"] = bf16_bits_to_f32(v_bits)
     return out
+
+
+def block_layout(heads: int, n: int, block_q: int, block_k: int, seed: int,
+                 density: float = 0.5, local: int = -1, global_cols: int = 0) -> np.ndarray:
+    """Block layout [heads, ceil(n/block_q), ceil(n/block_k)] uint8 (see recipe)."""
+    nq, nk = -(-n // block_q), -(-n // block_k)
+    rng = np.random.default_rng([seed, 8])
+    lay = (rng.random((heads, nq, nk)) < density).astype(np.uint8)
+    if local >= 0:
+        a = np.arange(nq)[:, None] * block_q // block_k   # key block on the diagonal
+        c = np.arange(nk)[None, :]
+        lay |= (np.abs(c - a) <= local).astype(np.uint8)[None]
+    if global_cols > 0:
+        lay[:, :, :global_cols] = 1
+    return lay
 
 
 def decode_lengths_and_table(B: int, H: int, d: int, page_size: int,

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"fa_fwd", "fa_decode", "fa_decode_workspace_bytes",
                           "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_varlen", "fa_fwd_paged",
-                          "fa_strerror", "fa_version"}
+                          "fa_fwd_blocksparse", "fa_strerror", "fa_version"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -179,4 +179,27 @@ def _paged_fwd(**kw):
 ])
 def test_paged_fwd_rejects(lib, kw, status):
     assert _paged_fwd(**kw) == status
+
+
+def _bsparse(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, lay=FAKE, lh=1, B=1, H=4, Hkv=2,
+                n=1000, d=128, bq=128, bk=64, causal=1, window=-1, scale=0.1, dtype=0)
+    args.update(kw)
+    return fa.lib().fa_fwd_blocksparse(args["q"], args["k"], args["v"], args["o"], args["lse"],
+                                       args["lay"], args["lh"], args["B"], args["H"],
+                                       args["Hkv"], args["n"], args["d"], args["bq"],
+                                       args["bk"], args["causal"], args["window"],
+                                       ctypes.c_float(args["scale"]), args["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(o=None), -1),
+    (dict(lse=None), -1), (dict(lay=None), -1),
+    (dict(B=0), -2), (dict(H=0), -2), (dict(n=0), -2), (dict(H=3, Hkv=2), -2),
+    (dict(lh=2), -2), (dict(lh=0), -2), (dict(causal=2), -2), (dict(scale=0.0), -2),
+    (dict(n=131073), -3), (dict(d=96), -3), (dict(bq=64), -3), (dict(bk=32), -3),
+    (dict(bk=256), -3), (dict(dtype=1), -3),
+])
+def test_blocksparse_rejects(lib, kw, status):
+    assert _bsparse(**kw) == status
 
