@@ -212,6 +212,8 @@ def time_other_workloads(fa, torch, np, bf, stream, reps: int = 20):
 
 VARLEN = dict(B=16, H=32, Hkv=8, d=128, min_len=1024, max_len=16384, seed=11)
 PAGED = dict(B=16, H=32, Hkv=8, d=128, prefix=(1024, 32768), chunk=(2048, 2048), seed=12)
+BLOCKSPARSE = {"H": 32, "Hkv": 8, "n": 32768, "d": 128, "density": 0.1, "local": 2,
+               "global": 1, "seed": 13}
 
 
 def _time(torch, stream, f, reps):
@@ -279,7 +281,49 @@ def time_ragged_workloads(fa, torch, np, bf, stream, reps: int = 20):
     log(f"{res[-1]['workload']}: {ms:.4f} ms  {tf:.1f} TFLOP/s in-band")
     del q, kc, vc, o, lse
     torch.cuda.empty_cache()
+
+    from io_aware_exact_fa_amd.inputs import block_layout, prefill_inputs
+    c = BLOCKSPARSE
+    inp = prefill_inputs(1, c["H"], c["Hkv"], c["n"], c["d"], seed=c["seed"])
+    q, k, v = bf(inp["q_bits"]), bf(inp["k_bits"]), bf(inp["v_bits"])
+    lay_np = block_layout(c["H"], c["n"], 128, 64, seed=c["seed"], density=c["density"],
+                          local=c["local"], global_cols=c["global"])
+    lay = torch.from_numpy(lay_np).to(q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((1, c["H"], c["n"]), dtype=torch.float32, device=q.device)
+    ms = _time(torch, stream, lambda: fa.fa_fwd_blocksparse(
+        q, k, v, o, lse, lay, c["H"], 1, c["H"], c["Hkv"], c["n"], c["d"], 128, 64, 1, -1,
+        1.0 / math.sqrt(c["d"]), fa.FA_BF16, stream), reps)
+    pairs = blocksparse_causal_pairs(lay_np, c["n"], 128, 64)
+    tf = 4 * c["d"] * pairs / (ms * 1e-3) / 1e12
+    kept = float(lay_np.mean())
+    res.append({"workload": f"block-sparse causal prefill n{c['n']} H{c['H']}/Hkv{c['Hkv']} "
+                            f"d{c['d']}, 128x64 blocks: local +-{c['local']}, first "
+                            f"{c['global']} column, {c['density']:.0%} random "
+                            f"({kept:.1%} of blocks kept)",
+                "ms": round(ms, 4), "TFLOP/s": round(tf, 2),
+                "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+    log(f"{res[-1]['workload']}: {ms:.4f} ms  {tf:.1f} TFLOP/s in-band")
+    del q, k, v, o, lse, lay
+    torch.cuda.empty_cache()
     return res
+
+
+def blocksparse_causal_pairs(layout, n: int, block_q: int, block_k: int) -> int:
+    """Visible (query, key) pairs of a block layout under a causal mask."""
+    import numpy as np
+    total = 0
+    t = np.arange(block_q)
+    for lay in layout:
+        a, c = np.nonzero(lay)
+        r0 = a * block_q
+        k0 = c * block_k
+        rows = r0[:, None] + t[None, :]                     # [blocks, block_q]
+        kend = np.minimum(k0 + block_k, n)[:, None]         # exclusive
+        cnt = np.clip(np.minimum(rows + 1, kend) - k0[:, None], 0, None)
+        cnt[rows >= n] = 0
+        total += int(cnt.sum())
+    return total
 
 
 def time_backward(fa, torch, bf, stream, q, k, v, o, lse, scale, steps: int):
@@ -346,8 +390,8 @@ def main():
                     help="timed fa_bwd calls on the prefill workload (0: skip the backward)")
     ap.add_argument("--all-workloads", action="store_true",
                     help="also time every workload (fp32 n=256, causal n=4096, band n=32768, "
-                         "ragged batch, chunked prefill over pages) and print one line each "
-                         "to stderr")
+                         "ragged batch, chunked prefill over pages, block-sparse) and print "
+                         "one line each to stderr")
     args = ap.parse_args()
     if args.traffic_from:
         rec = traffic_from_counters(*args.traffic_from)
