@@ -38,3 +38,4 @@ from .attention_bwd import (  # noqa: F401
 )
 from .varlen import attention_paged_prefill, attention_varlen  # noqa: F401
 from .blocksparse import attention_block_sparse, attention_masked  # noqa: F401
+from .fp8 import decode_fwd_fp8, e4m3_to_float  # noqa: F401
