@@ -16,6 +16,7 @@
  *   fa_fwd_varlen  fa_fwd over a ragged batch packed without padding.
  *   fa_fwd_paged   chunked prefill: new query chunks over paged KV histories.
  *   fa_fwd_blocksparse  fa_fwd restricted to the kept blocks of a layout.
+ *   fa_decode_fp8  fa_decode over an FP8 (E4M3) key/value cache.
  *
  * Sources (web pages on IO-aware exact attention):
  *   - charles2530 blog "算子与编译器：FlashAttention 与长上下文": §1 (the
@@ -268,6 +269,30 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            int B, int H, int Hkv, int n, int d, int causal, int window,
            float scale, int dtype, void* workspace, size_t workspace_bytes,
            void* stream);
+
+/*
+ * fa_decode_fp8 -- fa_decode over an FP8 key/value cache (quantised KV,
+ * charles2530 blog "算子与编译器：FlashAttention 与长上下文" §9).
+ *
+ *   kcache, vcache  [num_pages, Hkv, page_size, d] uint8: OCP E4M3 bytes
+ *                   (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no
+ *                   infinities; S.1111.111 is NaN)
+ *   k_scale, v_scale [Hkv] float32, DEVICE: per key/value head
+ *                   dequantisation scales, k = byte * k_scale[g],
+ *                   v = byte * v_scale[g]
+ *   everything else as fa_decode (q bf16, page_table, seqlens, o bf16, lse,
+ *   workspace of fa_decode_workspace_bytes(B, H, max_seqlen, d) bytes).
+ *
+ * The result is decode attention over the dequantised keys and values; half
+ * the bytes of the bf16 cache are read.  Limits and errors as fa_decode, plus
+ * FA_ERR_NULL when k_scale or v_scale is NULL.
+ */
+int fa_decode_fp8(const void* q, const void* kcache, const void* vcache,
+                  const float* k_scale, const float* v_scale,
+                  const int32_t* page_table, const int32_t* seqlens, void* o,
+                  float* lse, int B, int H, int Hkv, int d, int num_pages,
+                  int page_size, int max_pages, int max_seqlen, float scale,
+                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* Human-readable text of a status code (static storage, never NULL). */
 const char* fa_strerror(int status);

@@ -65,6 +65,9 @@ def lib() -> ctypes.CDLL:
     L.fa_fwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                      i32, i32, i32, i32, f32, i32, vp]
     L.fa_fwd_blocksparse.restype = i32
+    L.fa_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                i32, i32, i32, f32, vp, sz, vp]
+    L.fa_decode_fp8.restype = i32
     L.fa_strerror.argtypes = [i32]
     L.fa_strerror.restype = ctypes.c_char_p
     L.fa_version.argtypes = []
@@ -141,6 +144,19 @@ def fa_fwd_blocksparse(q, k, v, o, lse, layout, layout_heads, B, H, Hkv, n, d, b
                                   float(scale), int(dtype), _stream(stream))
     if st != 0:
         raise FaError(st, "fa_fwd_blocksparse")
+
+
+def fa_decode_fp8(q, kcache, vcache, k_scale, v_scale, page_table, seqlens, o, lse, B, H,
+                  Hkv, d, num_pages, page_size, max_pages, max_seqlen, scale, workspace,
+                  workspace_bytes, stream=None) -> None:
+    """Raw C-ABI call; tensors or integer device addresses."""
+    st = lib().fa_decode_fp8(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(k_scale), _ptr(v_scale),
+                             _ptr(page_table), _ptr(seqlens), _ptr(o), _ptr(lse), int(B),
+                             int(H), int(Hkv), int(d), int(num_pages), int(page_size),
+                             int(max_pages), int(max_seqlen), float(scale), _ptr(workspace),
+                             int(workspace_bytes), _stream(stream))
+    if st != 0:
+        raise FaError(st, "fa_decode_fp8")
 
 
 def fa_decode_workspace_bytes(B, H, max_seqlen, d) -> int:
@@ -347,5 +363,34 @@ def flash_attn_blocksparse(q, k, v, layout, block_q: int = 128, block_k: int = 6
     lse = torch.empty((B, H, n), dtype=torch.float32, device=q.device)
     fa_fwd_blocksparse(q, k, v, o, lse, layout, lh, B, H, Hkv, n, d, block_q, block_k,
                        int(bool(causal)), int(window), scale, FA_BF16, stream)
+    return o, lse
+
+
+def flash_decode_fp8(q, kcache, vcache, k_scale, v_scale, page_table, seqlens,
+                     max_seqlen: int, scale: float | None = None, workspace=None,
+                     stream=None):
+    """q [B,H,d] bf16; caches [P,Hkv,ps,d] uint8 (E4M3 bytes); k_scale/v_scale
+    [Hkv] float32; table [B,maxp] / seqlens [B] int32 -> (o, lse)."""
+    import torch
+    _check_contig(q, kcache, vcache, k_scale, v_scale, page_table, seqlens)
+    B, H, d = q.shape
+    P, Hkv, ps, d2 = kcache.shape
+    if d2 != d or tuple(vcache.shape) != tuple(kcache.shape):
+        raise ValueError("cache shapes disagree with q")
+    if kcache.dtype != torch.uint8 or vcache.dtype != torch.uint8:
+        raise ValueError("FP8 caches are uint8 tensors of E4M3 bytes")
+    if k_scale.dtype != torch.float32 or v_scale.dtype != torch.float32 or \
+            k_scale.numel() != Hkv or v_scale.numel() != Hkv:
+        raise ValueError("k_scale and v_scale must be float32 [Hkv]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nbytes = fa_decode_workspace_bytes(B, H, max_seqlen, d)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    fa_decode_fp8(q, kcache, vcache, k_scale, v_scale, page_table, seqlens, o, lse, B, H, Hkv,
+                  d, P, ps, page_table.shape[1], max_seqlen, scale, workspace,
+                  workspace.numel() * workspace.element_size(), stream)
     return o, lse
 

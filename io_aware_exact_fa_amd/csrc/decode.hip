@@ -31,6 +31,15 @@
 //     its base-2 log-sum-exp to the workspace.
 //   * The merge kernel (4 waves per (b, h)) reads the valid splits of each
 //     (b, h) and writes bf16 output and the natural-log lse.
+//   * FP8 caches (quantised KV, charles2530 blog §9): keys and values are
+//     bytes in the OCP E4M3 format with one scale per KV head.  Every E4M3
+//     value is exact in bf16, so a page's bytes are loaded into registers
+//     one page ahead, widened with v_cvt_pk_f32_fp8 and fed to the same
+//     bf16 MFMAs (V goes through the same LDS buffers, written from
+//     registers); the key scale joins the score scale and the value scale
+//     multiplies the split's output.  Half the bytes of the bf16 cache move.
+
+#include <type_traits>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -44,6 +53,10 @@ struct DecodeArgs {
   const __bf16* q;
   const __bf16* kc;
   const __bf16* vc;
+  const unsigned char* kc8;  // FP8 caches (E4M3 bytes)
+  const unsigned char* vc8;
+  const float* k_scale;      // [Hkv] FP8 dequantisation scales
+  const float* v_scale;
   const int32_t* page_table;
   const int32_t* seqlens;
   float* ws_o;    // [B, H, max_splits, D]
@@ -76,7 +89,23 @@ __device__ __forceinline__ void dma16(const void* src, void* lds) {
                                    (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
-template <int D, int GP>
+// Eight E4M3 bytes (little-endian in two words) widened to bf16; exact, as
+// every E4M3 value has at most 4 significant bits and a bf16-range exponent.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(u32x2 w) {
+  bf16x8 r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[h], false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[h], true);
+    r[4 * h + 0] = (__bf16)lo[0];
+    r[4 * h + 1] = (__bf16)lo[1];
+    r[4 * h + 2] = (__bf16)hi[0];
+    r[4 * h + 3] = (__bf16)hi[1];
+  }
+  return r;
+}
+
+template <int D, int GP, bool FP8>
 __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeArgs a) {
   static_assert(D == 128, "decode kernel is written for head dim 128");
   constexpr int NC = D / 32;   // 32-dim chunks of the QK contraction
@@ -123,7 +152,11 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x4{};
   float m_ref = kNegInf, l_part = 0.f;
-  const float c2 = a.scale_log2;
+  float c2 = a.scale_log2, vmul = 1.f;
+  if constexpr (FP8) {
+    c2 *= a.k_scale[g];  // scores scale by the key scale
+    vmul = a.v_scale[g];  // the output by the value scale
+  }
 
   // V DMA: lane i of instruction j writes LDS slot 64*j + i (16 B), which holds
   // physical chunk slot%16 of page row slot/16.
@@ -143,6 +176,11 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
   struct PageK {
     bf16x8 k[NC];
   };
+  struct PageK8 {  // FP8: the page's key and value bytes held by this lane
+    u32x2 k[NC];
+    u32x2 v[4];
+  };
+  using PageRegs = typename std::conditional<FP8, PageK8, PageK>::type;
   auto phys_of = [&](int i) {
     int phys = __builtin_amdgcn_readlane(my_phys, i);
     return (phys < 0 || phys >= a.num_pages) ? -1 : phys;
@@ -150,29 +188,56 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
   // Page i: K into registers (MFMA A layout: token lane%16, dims 32c +
   // 8*(lane/16) .. +8) and V into the LDS buffer vdst by DMA.  An invalid page
   // id loads page 0 (in bounds) and its tokens are masked.
-  auto load_page = [&](int i, PageK& r, char* vdst) {
+  auto load_page = [&](int i, PageRegs& r, char* vdst) {
     int phys = phys_of(i);
     if (phys < 0) phys = 0;
     const size_t base = ((size_t)phys * a.Hkv + g) * kPage * D;
-    const __bf16* kp = a.kc + base;
-    const char* vp = reinterpret_cast<const char*>(a.vc + base);
+    if constexpr (FP8) {
+      (void)vdst;
+      const unsigned char* kp = a.kc8 + base;
+      const unsigned char* vp = a.vc8 + base;
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-      r.k[c] = *reinterpret_cast<const bf16x8*>(kp + col * D + 32 * c + 8 * grp);
+      for (int c = 0; c < NC; ++c)
+        r.k[c] = *reinterpret_cast<const u32x2*>(kp + col * D + 32 * c + 8 * grp);
+      // the bytes of the 16-byte bf16 slots the V DMA would have moved
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(vp + v_off[j], vdst + 1024 * j);
+      for (int j = 0; j < 4; ++j) r.v[j] = *reinterpret_cast<const u32x2*>(vp + v_off[j] / 2);
+    } else {
+      const __bf16* kp = a.kc + base;
+      const char* vp = reinterpret_cast<const char*>(a.vc + base);
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        r.k[c] = *reinterpret_cast<const bf16x8*>(kp + col * D + 32 * c + 8 * grp);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dma16(vp + v_off[j], vdst + 1024 * j);
+    }
   };
 
-  auto process_page = [&](int i, const PageK& r, const char* vsrc) {
+  auto process_page = [&](int i, const PageRegs& r, const char* vsrc) {
     const bool valid = phys_of(i) >= 0;
     const int tok0 = (p0 + wave + kDecodeWaves * i) * kPage;
     const int lim = valid ? L : tok0;  // tokens at or past lim are masked
     const bool tail = tok0 + kPage > lim;
 
+    bf16x8 kf[NC];
+    if constexpr (FP8) {
+      // V: widen and write the page into this wave's buffer, in the layout the
+      // DMA gives the bf16 cache (the reads below follow in program order).
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<bf16x8*>(const_cast<char*>(vsrc) + 1024 * j + 16 * lane) =
+            e4m3x8_to_bf16(r.v[j]);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) kf[c] = e4m3x8_to_bf16(r.k[c]);
+    } else {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) kf[c] = r.k[c];
+    }
+
     // S^T = K Q^T: lane (col q, grp) holds tokens 4*grp + rr of query q.
     f32x4 sc = f32x4{};
 #pragma unroll
-    for (int c = 0; c < NC; ++c) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.k[c], qf[c], sc, 0, 0, 0);
+    for (int c = 0; c < NC; ++c) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[c], qf[c], sc, 0, 0, 0);
     if (tail) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr)
@@ -221,7 +286,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
 
   // Two K register sets and two V buffers: page i+1 is in flight while page i
   // is processed.
-  PageK ka, kb;
+  PageRegs ka, kb;
   if (cnt > 0) load_page(0, ka, sV0[wave]);
   for (int i = 0; i < cnt; i += 2) {
     if (i + 1 < cnt) load_page(i + 1, kb, sV1[wave]);
@@ -267,7 +332,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
       osum = __builtin_fmaf(wt, wacc(w, qq, d), osum);
     }
     const size_t row = ((size_t)b * a.H + (size_t)g * G + qq) * a.max_splits + s;
-    a.ws_o[row * D + d] = wsum > 0.f ? osum / wsum : 0.f;
+    a.ws_o[row * D + d] = wsum > 0.f ? vmul * osum / wsum : 0.f;
     if (d == 0) a.ws_lse[row] = wsum > 0.f ? Mu + log2_fast(wsum) : kNegInf;
   }
 }
@@ -371,21 +436,37 @@ size_t decode_workspace_bytes(int B, int H, int max_seqlen, int d) {
   return align_up(rows * d * sizeof(float), 256) + align_up(rows * sizeof(float), 256);
 }
 
-template <int GP>
+template <int GP, bool FP8>
 static void launch_split(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<128, GP>), dim3(a.max_splits, a.Hkv, a.B),
+  hipLaunchKernelGGL((decode_split_kernel<128, GP, FP8>), dim3(a.max_splits, a.Hkv, a.B),
                      dim3(kDecodeWaves * 64), 0, stream, a);
 }
 
-hipError_t launch_decode(const void* q, const void* kcache, const void* vcache,
-                         const int32_t* page_table, const int32_t* seqlens, void* o, float* lse,
-                         int B, int H, int Hkv, int d, int num_pages, int max_pages,
-                         int max_seqlen, float scale, void* workspace, hipStream_t stream) {
-  if (d != 128) return hipErrorInvalidValue;
-  DecodeArgs a;
+template <bool FP8>
+static hipError_t launch_decode_t(DecodeArgs& a, int B, int H, int d, void* workspace,
+                                  hipStream_t stream) {
+  const size_t rows = (size_t)B * H * a.max_splits;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                      align_up(rows * d * sizeof(float), 256));
+  const int G = a.G;
+  if (G <= 1) launch_split<1, FP8>(a, stream);
+  else if (G <= 2) launch_split<2, FP8>(a, stream);
+  else if (G <= 4) launch_split<4, FP8>(a, stream);
+  else if (G <= 8) launch_split<8, FP8>(a, stream);
+  else if (G <= 16) launch_split<16, FP8>(a, stream);
+  else return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(B * H), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+static DecodeArgs decode_args(const void* q, const int32_t* page_table, const int32_t* seqlens,
+                              void* o, float* lse, int B, int H, int Hkv, int num_pages,
+                              int max_pages, int max_seqlen, float scale) {
+  DecodeArgs a{};
   a.q = static_cast<const __bf16*>(q);
-  a.kc = static_cast<const __bf16*>(kcache);
-  a.vc = static_cast<const __bf16*>(vcache);
   a.page_table = page_table;
   a.seqlens = seqlens;
   a.o = static_cast<__bf16*>(o);
@@ -395,21 +476,35 @@ hipError_t launch_decode(const void* q, const void* kcache, const void* vcache,
   a.split_pages = decode_split_pages(B, H, max_seqlen);
   a.max_splits = decode_max_splits(B, H, max_seqlen);
   a.scale_log2 = scale * kLog2e;
-  const size_t rows = (size_t)B * H * a.max_splits;
-  a.ws_o = static_cast<float*>(workspace);
-  a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                      align_up(rows * d * sizeof(float), 256));
-  const int G = a.G;
-  if (G <= 1) launch_split<1>(a, stream);
-  else if (G <= 2) launch_split<2>(a, stream);
-  else if (G <= 4) launch_split<4>(a, stream);
-  else if (G <= 8) launch_split<8>(a, stream);
-  else if (G <= 16) launch_split<16>(a, stream);
-  else return hipErrorInvalidValue;
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(B * H), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  return a;
+}
+
+hipError_t launch_decode_fp8(const void* q, const void* kcache, const void* vcache,
+                             const float* k_scale, const float* v_scale,
+                             const int32_t* page_table, const int32_t* seqlens, void* o,
+                             float* lse, int B, int H, int Hkv, int d, int num_pages,
+                             int max_pages, int max_seqlen, float scale, void* workspace,
+                             hipStream_t stream) {
+  if (d != 128) return hipErrorInvalidValue;
+  DecodeArgs a = decode_args(q, page_table, seqlens, o, lse, B, H, Hkv, num_pages, max_pages,
+                             max_seqlen, scale);
+  a.kc8 = static_cast<const unsigned char*>(kcache);
+  a.vc8 = static_cast<const unsigned char*>(vcache);
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  return launch_decode_t<true>(a, B, H, d, workspace, stream);
+}
+
+hipError_t launch_decode(const void* q, const void* kcache, const void* vcache,
+                         const int32_t* page_table, const int32_t* seqlens, void* o, float* lse,
+                         int B, int H, int Hkv, int d, int num_pages, int max_pages,
+                         int max_seqlen, float scale, void* workspace, hipStream_t stream) {
+  if (d != 128) return hipErrorInvalidValue;
+  DecodeArgs a = decode_args(q, page_table, seqlens, o, lse, B, H, Hkv, num_pages, max_pages,
+                             max_seqlen, scale);
+  a.kc = static_cast<const __bf16*>(kcache);
+  a.vc = static_cast<const __bf16*>(vcache);
+  return launch_decode_t<false>(a, B, H, d, workspace, stream);
 }
 
 }  // namespace fa

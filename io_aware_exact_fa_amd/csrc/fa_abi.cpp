@@ -21,7 +21,7 @@ bool fits_i32(long long x) { return x >= 0 && x < (long long)INT_MAX; }
 
 extern "C" {
 
-int fa_version(void) { return (1 << 16) | 3; }
+int fa_version(void) { return (1 << 16) | 4; }
 
 const char* fa_strerror(int status) {
   switch (status) {
@@ -155,6 +155,28 @@ int fa_decode(const void* q, const void* kcache, const void* vcache, const int32
   hipError_t e = fa::launch_decode(q, kcache, vcache, page_table, seqlens, o, lse, B, H, Hkv, d,
                                    num_pages, max_pages, max_seqlen, scale, workspace,
                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_decode_fp8(const void* q, const void* kcache, const void* vcache, const float* k_scale,
+                  const float* v_scale, const int32_t* page_table, const int32_t* seqlens,
+                  void* o, float* lse, int B, int H, int Hkv, int d, int num_pages,
+                  int page_size, int max_pages, int max_seqlen, float scale, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  if (!q || !kcache || !vcache || !k_scale || !v_scale || !page_table || !seqlens || !o || !lse)
+    return FA_ERR_NULL;
+  if (B < 1 || H < 1 || Hkv < 1 || d < 1 || num_pages < 1 || page_size < 1 || max_pages < 1 ||
+      max_seqlen < 1)
+    return FA_ERR_SHAPE;
+  if (H % Hkv != 0) return FA_ERR_SHAPE;
+  if (!scale_ok(scale)) return FA_ERR_SHAPE;
+  if (!fits_i32((long long)B * H) || !fits_i32((long long)B * max_pages)) return FA_ERR_SHAPE;
+  if (d != 128 || page_size != 16 || H / Hkv > 16) return FA_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < fa::decode_workspace_bytes(B, H, max_seqlen, d))
+    return FA_ERR_WORKSPACE;
+  hipError_t e = fa::launch_decode_fp8(q, kcache, vcache, k_scale, v_scale, page_table, seqlens,
+                                       o, lse, B, H, Hkv, d, num_pages, max_pages, max_seqlen,
+                                       scale, workspace, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -42,6 +42,13 @@ hipError_t launch_prefill_f32(const void* q, const void* k, const void* v, void*
 int decode_split_pages(int B, int H, int max_seqlen);
 int decode_max_splits(int B, int H, int max_seqlen);
 size_t decode_workspace_bytes(int B, int H, int max_seqlen, int d);
+// FP8 decode: caches of E4M3 bytes, scales [Hkv] (device).
+hipError_t launch_decode_fp8(const void* q, const void* kcache, const void* vcache,
+                             const float* k_scale, const float* v_scale,
+                             const int32_t* page_table, const int32_t* seqlens, void* o,
+                             float* lse, int B, int H, int Hkv, int d, int num_pages,
+                             int max_pages, int max_seqlen, float scale, void* workspace,
+                             hipStream_t stream);
 hipError_t launch_decode(const void* q, const void* kcache, const void* vcache,
                          const int32_t* page_table, const int32_t* seqlens, void* o,
                          float* lse, int B, int H, int Hkv, int d, int num_pages,

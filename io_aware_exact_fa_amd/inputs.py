@@ -30,6 +30,10 @@ Recipe (fixed so every consumer sees bit-identical inputs):
     plus (optionally) a local band of ``local`` key blocks on each side of the
     diagonal (block indices scaled by block_q / block_k) and the first
     ``global_cols`` key-block columns;
+  * FP8 decode: lengths, q and page table as decode; sequence b's K and V
+    draws come from the same generators as decode, divided by the per-head
+    scale (k_scale[g] = (1 + g/16)/8, v_scale[g] = (1 + g/32)/8) and rounded to
+    the nearest OCP E4M3 byte (ties to even, clipped to +-448);
   * bf16 storage: round-to-nearest-even of the float32 draw to bfloat16;
     the returned float32 arrays hold exactly the rounded values;
   * decode: from ``default_rng(seed)``: the sequence lengths (discrete uniform
@@ -58,6 +62,8 @@ __all__ = [
     "varlen_inputs",
     "paged_prefill_inputs",
     "block_layout",
+    "fp8_scales",
+    "decode_fp8_inputs",
     "decode_lengths_and_table",
     "decode_sequence_kv",
     "decode_inputs",
@@ -283,3 +289,42 @@ def decode_inputs(B: int, H: int, Hkv: int, d: int, page_size: int,
         meta["kcache"] = bf16_bits_to_f32(k_bits)
         meta["vcache"] = bf16_bits_to_f32(v_bits)
     return meta
+
+
+def fp8_scales(Hkv: int):
+    """Per key/value head FP8 scales (k_scale, v_scale), float32 [Hkv]."""
+    g = np.arange(Hkv, dtype=np.float64)
+    return ((1 + g / 16) / 8).astype(np.float32), ((1 + g / 32) / 8).astype(np.float32)
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """Nearest OCP E4M3 byte of float32 values (ties to even, clipped to +-448)."""
+    import torch
+    t = torch.from_numpy(np.clip(np.asarray(x, dtype=np.float32), -448.0, 448.0))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def decode_fp8_inputs(B: int, H: int, Hkv: int, d: int, page_size: int,
+                      min_len: int, max_len: int, seed: int, seqlens=None) -> dict:
+    """Paged decode workload with E4M3 caches: as ``decode_inputs`` (lengths,
+    q, table) plus ``kcache8``/``vcache8`` [P, Hkv, page_size, d] uint8 and
+    ``k_scale``/``v_scale`` [Hkv] float32."""
+    meta = decode_lengths_and_table(B, H, d, page_size, min_len, max_len, seed, seqlens=seqlens)
+    P = meta["num_pages"]
+    ks, vs = fp8_scales(Hkv)
+    k8 = np.empty((P, Hkv, page_size, d), dtype=np.uint8)
+    v8 = np.empty_like(k8)
+
+    def fill(b):
+        pb = int(meta["pages"][b])
+        kx = _draw(np.random.default_rng([seed, 1, b]), (pb, Hkv, page_size, d), 1.0)
+        vx = _draw(np.random.default_rng([seed, 2, b]), (pb, Hkv, page_size, d), 1.0)
+        phys = meta["page_table"][b, :pb]
+        k8[phys] = e4m3_encode(kx / ks[None, :, None, None])
+        v8[phys] = e4m3_encode(vx / vs[None, :, None, None])
+
+    with ThreadPoolExecutor(max_workers=max(1, min(8, os.cpu_count() or 1))) as ex:
+        list(ex.map(fill, range(B)))
+    meta.update(kcache8=k8, vcache8=v8, k_scale=ks, v_scale=vs)
+    return meta
+

@@ -18,7 +18,7 @@ FAKE = 256  # a non-NULL address that validation rejects before any use
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -32,7 +32,8 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"fa_fwd", "fa_decode", "fa_decode_workspace_bytes",
                           "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_varlen", "fa_fwd_paged",
-                          "fa_fwd_blocksparse", "fa_strerror", "fa_version"}
+                          "fa_fwd_blocksparse", "fa_decode_fp8", "fa_strerror",
+                          "fa_version"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -202,4 +203,29 @@ def _bsparse(**kw):
 ])
 def test_blocksparse_rejects(lib, kw, status):
     assert _bsparse(**kw) == status
+
+
+def _dec8(**kw):
+    args = dict(q=FAKE, kc=FAKE, vc=FAKE, ks=FAKE, vs=FAKE, pt=FAKE, sl=FAKE, o=FAKE, lse=FAKE,
+                B=2, H=8, Hkv=2, d=128, P=10, ps=16, maxp=4, maxs=64, scale=0.1, ws=FAKE,
+                wsb=1 << 30)
+    args.update(kw)
+    return fa.lib().fa_decode_fp8(args["q"], args["kc"], args["vc"], args["ks"], args["vs"],
+                                  args["pt"], args["sl"], args["o"], args["lse"], args["B"],
+                                  args["H"], args["Hkv"], args["d"], args["P"], args["ps"],
+                                  args["maxp"], args["maxs"], ctypes.c_float(args["scale"]),
+                                  args["ws"], args["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(kc=None), -1), (dict(vc=None), -1), (dict(ks=None), -1),
+    (dict(vs=None), -1), (dict(pt=None), -1), (dict(sl=None), -1), (dict(o=None), -1),
+    (dict(lse=None), -1),
+    (dict(B=0), -2), (dict(H=0), -2), (dict(Hkv=0), -2), (dict(P=0), -2), (dict(maxs=0), -2),
+    (dict(H=6, Hkv=4), -2), (dict(scale=-1.0), -2),
+    (dict(d=64), -3), (dict(ps=8), -3), (dict(H=34, Hkv=2), -3),
+    (dict(ws=None), -4), (dict(wsb=16), -4),
+])
+def test_decode_fp8_rejects(lib, kw, status):
+    assert _dec8(**kw) == status
 
