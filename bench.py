@@ -309,6 +309,41 @@ def time_ragged_workloads(fa, torch, np, bf, stream, reps: int = 20):
     return res
 
 
+def time_decode_fp8(fa, torch, np, bf, stream, reps: int = 20):
+    """The paged decode workload with an E4M3 cache (per-head scales)."""
+    from io_aware_exact_fa_amd.inputs import decode_fp8_inputs
+    Dc = DECODE
+    meta = decode_fp8_inputs(Dc["B"], Dc["H"], Dc["Hkv"], Dc["d"], Dc["page_size"],
+                             Dc["min_len"], Dc["max_len"], seed=Dc["seed"])
+    dev = torch.device("cuda")
+    q = bf(meta["q_bits"])
+    kc = torch.from_numpy(meta["kcache8"]).to(dev)
+    vc = torch.from_numpy(meta["vcache8"]).to(dev)
+    ks = torch.from_numpy(meta["k_scale"]).to(dev)
+    vs = torch.from_numpy(meta["v_scale"]).to(dev)
+    pt = torch.from_numpy(meta["page_table"]).to(dev)
+    sl = torch.from_numpy(meta["seqlens"]).to(dev)
+    del meta["kcache8"], meta["vcache8"]
+    o = torch.empty_like(q)
+    lse = torch.empty((Dc["B"], Dc["H"]), dtype=torch.float32, device=dev)
+    ws_bytes = fa.fa_decode_workspace_bytes(Dc["B"], Dc["H"], Dc["max_len"], Dc["d"])
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ms = _time(torch, stream, lambda: fa.fa_decode_fp8(
+        q, kc, vc, ks, vs, pt, sl, o, lse, Dc["B"], Dc["H"], Dc["Hkv"], Dc["d"], kc.shape[0],
+        Dc["page_size"], pt.shape[1], Dc["max_len"], 1.0 / math.sqrt(Dc["d"]), ws, ws_bytes,
+        stream), reps)
+    kv_bytes = int(np.sum(meta["seqlens"].astype(np.int64))) * Dc["Hkv"] * Dc["d"] * 2
+    gbs = kv_bytes / (ms * 1e-3) / 1e9
+    rec = {"workload": "paged decode B64 H32/Hkv8 d128 L~U[1024,32768] page16, E4M3 K/V "
+                       "cache with per-head scales",
+           "ms": round(ms, 4), "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+           "kv_bytes": kv_bytes}
+    log(f"{rec['workload']}: {ms:.4f} ms  {gbs:.0f} GB/s of KV")
+    del q, kc, vc, o, lse, ws
+    torch.cuda.empty_cache()
+    return [rec]
+
+
 def blocksparse_causal_pairs(layout, n: int, block_q: int, block_k: int) -> int:
     """Visible (query, key) pairs of a block layout under a causal mask."""
     import numpy as np
@@ -390,8 +425,8 @@ def main():
                     help="timed fa_bwd calls on the prefill workload (0: skip the backward)")
     ap.add_argument("--all-workloads", action="store_true",
                     help="also time every workload (fp32 n=256, causal n=4096, band n=32768, "
-                         "ragged batch, chunked prefill over pages, block-sparse) and print "
-                         "one line each to stderr")
+                         "ragged batch, chunked prefill over pages, block-sparse, FP8 decode) "
+                         "and print one line each to stderr")
     args = ap.parse_args()
     if args.traffic_from:
         rec = traffic_from_counters(*args.traffic_from)
@@ -538,7 +573,8 @@ def main():
     torch.cuda.empty_cache()
     if args.all_workloads:
         out["other_workloads"] = (time_other_workloads(fa, torch, np, bf, stream) +
-                                  time_ragged_workloads(fa, torch, np, bf, stream))
+                                  time_ragged_workloads(fa, torch, np, bf, stream) +
+                                  time_decode_fp8(fa, torch, np, bf, stream))
     log("timing the oracle on a bounded sample")
     out["cpu_baseline"] = cpu_baseline(pin, max(1, args.cpu_rows),
                                        heads=[0, 5, 10, 15, 16, 21, 26, 31])
