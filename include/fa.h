@@ -17,6 +17,7 @@
  *   fa_fwd_paged   chunked prefill: new query chunks over paged KV histories.
  *   fa_fwd_blocksparse  fa_fwd restricted to the kept blocks of a layout.
  *   fa_decode_fp8  fa_decode over an FP8 (E4M3) key/value cache.
+ *   fa_fwd_strided fa_fwd over caller-strided tensors (e.g. BSHD).
  *
  * Sources (web pages on IO-aware exact attention):
  *   - charles2530 blog "算子与编译器：FlashAttention 与长上下文": §1 (the
@@ -189,6 +190,27 @@ int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, flo
                        const uint8_t* layout, int layout_heads, int B, int H, int Hkv,
                        int n, int d, int block_q, int block_k, int causal, int window,
                        float scale, int dtype, void* stream);
+
+/*
+ * fa_fwd_strided -- fa_fwd with caller-given strides (for instance the
+ * (batch, seqlen, heads, head_dim) layout of the library call described in
+ * the xxqk.cn sliding-window prefill article §7.1, or q/k/v views into one
+ * packed qkv tensor).
+ *
+ *   strides  HOST array of 12 int64, in ELEMENTS:
+ *            q (batch, head, row), k (batch, head, row), v (batch, head, row),
+ *            o (batch, head, row); element [b][h][i][t] of q is at
+ *            q + b*strides[0] + h*strides[1] + i*strides[2] + t.
+ *   lse      [B, H, n] float32, contiguous (as fa_fwd).
+ * The head dim is contiguous; k and v must share their row stride; every
+ * stride is >= 0, a multiple of 8 elements, and row strides are >= d; base
+ * pointers are 16-byte aligned.  Otherwise as fa_fwd (bf16 only).
+ * Errors: FA_ERR_NULL (also strides NULL), FA_ERR_SHAPE (also bad strides),
+ * FA_ERR_UNSUPPORTED, FA_ERR_LAUNCH.
+ */
+int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                   const int64_t* strides, int B, int H, int Hkv, int n, int d,
+                   int causal, int window, float scale, int dtype, void* stream);
 
 /*
  * fa_decode_workspace_bytes -- device workspace fa_decode needs for these

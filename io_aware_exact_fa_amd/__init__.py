@@ -12,5 +12,6 @@ from .binding import (  # noqa: F401
     fa_fwd, fa_decode, fa_decode_workspace_bytes, fa_bwd, fa_bwd_workspace_bytes,
     fa_fwd_varlen, fa_fwd_paged, fa_strerror, fa_version, flash_attn_fwd, flash_decode,
     flash_attn_bwd, flash_attn_varlen, flash_attn_paged, fa_fwd_blocksparse,
-    flash_attn_blocksparse, fa_decode_fp8, flash_decode_fp8,
+    flash_attn_blocksparse, fa_decode_fp8, flash_decode_fp8, fa_fwd_strided,
+    flash_attn_strided,
 )

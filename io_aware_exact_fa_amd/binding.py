@@ -68,6 +68,9 @@ def lib() -> ctypes.CDLL:
     L.fa_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                 i32, i32, i32, f32, vp, sz, vp]
     L.fa_decode_fp8.restype = i32
+    L.fa_fwd_strided.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                 f32, i32, vp]
+    L.fa_fwd_strided.restype = i32
     L.fa_strerror.argtypes = [i32]
     L.fa_strerror.restype = ctypes.c_char_p
     L.fa_version.argtypes = []
@@ -157,6 +160,18 @@ def fa_decode_fp8(q, kcache, vcache, k_scale, v_scale, page_table, seqlens, o, l
                              int(workspace_bytes), _stream(stream))
     if st != 0:
         raise FaError(st, "fa_decode_fp8")
+
+
+def fa_fwd_strided(q, k, v, o, lse, strides, B, H, Hkv, n, d, causal, window, scale, dtype,
+                   stream=None) -> None:
+    """Raw C-ABI call; ``strides`` is a sequence of 12 element strides."""
+    arr = (ctypes.c_int64 * 12)(*[int(x) for x in strides])
+    st = lib().fa_fwd_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                              ctypes.cast(arr, ctypes.c_void_p), int(B), int(H), int(Hkv),
+                              int(n), int(d), int(causal), int(window), float(scale), int(dtype),
+                              _stream(stream))
+    if st != 0:
+        raise FaError(st, "fa_fwd_strided")
 
 
 def fa_decode_workspace_bytes(B, H, max_seqlen, d) -> int:
@@ -393,4 +408,36 @@ def flash_decode_fp8(q, kcache, vcache, k_scale, v_scale, page_table, seqlens,
                   d, P, ps, page_table.shape[1], max_seqlen, scale, workspace,
                   workspace.numel() * workspace.element_size(), stream)
     return o, lse
+
+
+def flash_attn_strided(q, k, v, causal: bool = False, window: int = -1,
+                       scale: float | None = None, out=None, stream=None, layout: str = "bhsd"):
+    """Attention over strided bf16 views.
+
+    ``layout`` names how the four dims of q, k, v (and ``out``) are ordered:
+    "bhsd" (batch, heads, seq, dim) or "bshd" (batch, seq, heads, dim, the
+    layout of the library call in the sources).  Any strides are accepted as
+    long as the head dim is contiguous (e.g. views into a packed qkv tensor).
+    Returns (o in the same layout as q, lse [B, H, n] float32).
+    """
+    import torch
+    if layout not in ("bhsd", "bshd"):
+        raise ValueError("layout must be 'bhsd' or 'bshd'")
+    perm = (0, 1, 2, 3) if layout == "bhsd" else (0, 2, 1, 3)
+    qv, kv_, vv = (t.permute(*perm) for t in (q, k, v))  # -> [B, heads, n, d] views
+    B, H, n, d = qv.shape
+    Hkv = kv_.shape[1]
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16 or t.stride(-1) != 1:
+            raise ValueError("bf16 tensors with a contiguous head dim are required")
+    if out is None:
+        out = torch.empty_like(q)
+    ov = out.permute(*perm)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    lse = torch.empty((B, H, n), dtype=torch.float32, device=q.device)
+    strides = [*qv.stride()[:3], *kv_.stride()[:3], *vv.stride()[:3], *ov.stride()[:3]]
+    fa_fwd_strided(q, k, v, out, lse, strides, B, H, Hkv, n, d, int(bool(causal)), int(window),
+                   scale, FA_BF16, stream)
+    return out, lse
 

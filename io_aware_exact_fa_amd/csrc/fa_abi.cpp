@@ -21,7 +21,7 @@ bool fits_i32(long long x) { return x >= 0 && x < (long long)INT_MAX; }
 
 extern "C" {
 
-int fa_version(void) { return (1 << 16) | 4; }
+int fa_version(void) { return (1 << 16) | 5; }
 
 const char* fa_strerror(int status) {
   switch (status) {
@@ -78,6 +78,32 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
   hipError_t e = fa::launch_prefill_bf16_varlen(q, k, v, o, lse, cu_seqlens, B, H, Hkv, total,
                                                 max_seqlen, d, causal, window, scale,
                                                 static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                   const int64_t* strides, int B, int H, int Hkv, int n, int d, int causal,
+                   int window, float scale, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse || !strides) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || Hkv < 1 || n < 1 || d < 1) return FA_ERR_SHAPE;
+  if (H % Hkv != 0) return FA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
+  if (!scale_ok(scale)) return FA_ERR_SHAPE;
+  if (!fits_i32((long long)n * d) || !fits_i32((long long)B * H)) return FA_ERR_SHAPE;
+  for (int i = 0; i < 12; ++i)
+    if (strides[i] < 0 || strides[i] % 8 != 0) return FA_ERR_SHAPE;
+  const long long rs[4] = {strides[2], strides[5], strides[8], strides[11]};
+  for (long long r : rs)
+    if (r < d || r > (1LL << 24)) return FA_ERR_SHAPE;
+  if (strides[5] != strides[8]) return FA_ERR_SHAPE;  // k and v row strides
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (window < 0) window = -1;
+  if (window > n) window = n;
+  long long st[12];
+  for (int i = 0; i < 12; ++i) st[i] = strides[i];
+  hipError_t e = fa::launch_prefill_bf16_strided(q, k, v, o, lse, st, B, H, Hkv, n, d, causal,
+                                                 window, scale, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

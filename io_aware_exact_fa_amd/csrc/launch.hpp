@@ -34,6 +34,12 @@ hipError_t launch_prefill_bf16_blocksparse(const void* q, const void* k, const v
                                            int layout_heads, int B, int H, int Hkv, int n, int d,
                                            int block_k, int causal, int window, float scale,
                                            hipStream_t stream);
+// Strided dense problem: strides[12] (elements) = q (batch, head, row), k (...),
+// v (...), o (...); k and v share the row stride.
+hipError_t launch_prefill_bf16_strided(const void* q, const void* k, const void* v, void* o,
+                                       float* lse, const long long* strides, int B, int H,
+                                       int Hkv, int n, int d, int causal, int window, float scale,
+                                       hipStream_t stream);
 hipError_t launch_prefill_f32(const void* q, const void* k, const void* v, void* o,
                               float* lse, int B, int H, int Hkv, int n, int d,
                               int causal, int window, float scale, hipStream_t stream);

@@ -63,7 +63,12 @@ namespace fa {
 //            all); a workgroup visits only its kept key tiles ("Block-Sparse
 //            FlashAttention", ruiowl.com deep-dive §四; the band skip of the
 //            xxqk.cn article §5 is the case of a band layout).
-enum PrefillMode { kDense = 0, kVarlen = 1, kPaged = 2, kBlockSparse = 3 };
+//   kStrided: the dense problem with caller-given element strides for
+//            (batch, head, row) of q, k, v and o, the head dim contiguous (for
+//            instance the (batch, seqlen, heads, head_dim) layout of the
+//            library call in the xxqk.cn article §7.1); k and v share a row
+//            stride.  lse stays [B, H, n].
+enum PrefillMode { kDense = 0, kVarlen = 1, kPaged = 2, kBlockSparse = 3, kStrided = 4 };
 
 // Most key tiles a block-sparse workgroup can list (n <= 2048 * 64).
 constexpr int kMaxSparseTiles = 2048;
@@ -88,6 +93,9 @@ struct PrefillArgs {
   // kBlockSparse
   const unsigned char* layout;
   int layout_heads, layout_cols, tile_shift;  // tile_shift: log2(block_k / 64)
+  // kStrided: element strides (batch, head) and row strides
+  long long q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;
+  int q_ss, kv_ss, o_ss;
 };
 
 // LDS tiles are dense (no padding): row r of a tile holds D bf16 values as
@@ -186,9 +194,21 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a)
   const __bf16 *Qh, *Kh = nullptr, *Vh = nullptr;
   __bf16* Oh;
   float* Lh;
-  static_assert(MODE == kDense || MODE == kVarlen || MODE == kPaged || MODE == kBlockSparse,
+  static_assert(MODE == kDense || MODE == kVarlen || MODE == kPaged || MODE == kBlockSparse ||
+                    MODE == kStrided,
                 "unknown layout mode");
-  if constexpr (MODE == kDense || MODE == kBlockSparse) {  // [B, heads, n, d]
+  // Row strides in elements (the head dim is contiguous in every layout).
+  const int q_rs = MODE == kStrided ? a.q_ss : D;
+  const int kv_rs = MODE == kStrided ? a.kv_ss : D;
+  const int o_rs = MODE == kStrided ? a.o_ss : D;
+  if constexpr (MODE == kStrided) {
+    n_q = n_k = a.n;
+    Qh = a.q + b * a.q_sb + h * a.q_sh;
+    Kh = a.k + b * a.k_sb + g * a.k_sh;
+    Vh = a.v + b * a.v_sb + g * a.v_sh;
+    Oh = a.o + b * a.o_sb + h * a.o_sh;
+    Lh = a.lse + (size_t)(b * a.H + h) * a.n;
+  } else if constexpr (MODE == kDense || MODE == kBlockSparse) {  // [B, heads, n, d]
     n_q = n_k = a.n;
     Qh = a.q + (size_t)(b * a.H + h) * a.n * D;
     Kh = a.k + (size_t)(b * a.Hkv + g) * a.n * D;
@@ -240,7 +260,8 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a)
   bf16x8 qf[NDC];
 #pragma unroll
   for (int dc = 0; dc < NDC; ++dc)
-    qf[dc] = (row < n_q) ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)row * D + dc * 16 + hi * 8)
+    qf[dc] = (row < n_q) ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)row * q_rs + dc * 16 +
+                                                             hi * 8)
                          : bf16x8{};
 
   f32x16 acc[NDB];
@@ -264,7 +285,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a)
     const int s = (wave_u * IPW + j) * 64 + lane;
     const int r = s / CPR;
     const int c = (s % CPR) ^ swz<D>(r);
-    st_off[j] = (unsigned)(r * RB + c * 16);
+    st_off[j] = (unsigned)(r * kv_rs * 2 + c * 16);
     st_row[j] = r;
   }
   // Paged tiles: the four page ids of tile kt (pages past the sequence's
@@ -285,9 +306,12 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a)
     const int k0 = kt * BC;
     if constexpr (MODE != kPaged) {
       (void)pid;
-      const int bytes = (n_k - k0) * RB;
-      const __bf16* kb = Kh + (size_t)k0 * D;
-      const __bf16* vb = Vh + (size_t)k0 * D;
+      // the descriptor ends after the tile's last row inside the sequence:
+      // later rows read as zero (their offsets lie beyond it, as rows are at
+      // least a row apart)
+      const int bytes = (min(n_k - k0, BC) - 1) * kv_rs * 2 + RB;
+      const __bf16* kb = Kh + (size_t)k0 * kv_rs;
+      const __bf16* vb = Vh + (size_t)k0 * kv_rs;
 #pragma unroll
       for (int j = 0; j < IPW; ++j) {
         buffer_load_lds16(kb, bytes, st_off[j], tk + (wave_u * IPW + j) * 1024);
@@ -497,7 +521,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a)
   // lt = 0 only for a row that sees no key (a chunk longer than its
   // sequence's keys): o = 0, lse = -inf.
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  __bf16* orow = Oh + (size_t)row * D;
+  __bf16* orow = Oh + (size_t)row * o_rs;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -578,6 +602,21 @@ hipError_t launch_prefill_bf16_blocksparse(const void* q, const void* k, const v
   a.tile_shift = block_k == 128 ? 1 : 0;
   if (d == 128) return launch_d<128, kBlockSparse>(a, n, stream);
   if (d == 64) return launch_d<64, kBlockSparse>(a, n, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_bf16_strided(const void* q, const void* k, const void* v, void* o,
+                                       float* lse, const long long* strides, int B, int H,
+                                       int Hkv, int n, int d, int causal, int window, float scale,
+                                       hipStream_t stream) {
+  PrefillArgs a = base_args(q, k, v, o, lse, B, H, Hkv, causal, window, scale);
+  a.n = n;
+  a.q_sb = strides[0]; a.q_sh = strides[1]; a.q_ss = (int)strides[2];
+  a.k_sb = strides[3]; a.k_sh = strides[4]; a.kv_ss = (int)strides[5];
+  a.v_sb = strides[6]; a.v_sh = strides[7];
+  a.o_sb = strides[9]; a.o_sh = strides[10]; a.o_ss = (int)strides[11];
+  if (d == 128) return launch_d<128, kStrided>(a, n, stream);
+  if (d == 64) return launch_d<64, kStrided>(a, n, stream);
   return hipErrorInvalidValue;
 }
 

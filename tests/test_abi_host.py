@@ -32,8 +32,8 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"fa_fwd", "fa_decode", "fa_decode_workspace_bytes",
                           "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_varlen", "fa_fwd_paged",
-                          "fa_fwd_blocksparse", "fa_decode_fp8", "fa_strerror",
-                          "fa_version"}
+                          "fa_fwd_blocksparse", "fa_decode_fp8", "fa_fwd_strided",
+                          "fa_strerror", "fa_version"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -228,4 +228,42 @@ def _dec8(**kw):
 ])
 def test_decode_fp8_rejects(lib, kw, status):
     assert _dec8(**kw) == status
+
+
+def _strided(strides=None, **kw):
+    B, H, n, d = 2, 4, 100, 128
+    if strides is None:  # BSHD
+        strides = [n * H * d, d, H * d, n * 2 * d, d, 2 * d, n * 2 * d, d, 2 * d,
+                   n * H * d, d, H * d]
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=B, H=H, Hkv=2, n=n, d=d, causal=1,
+                window=-1, scale=0.1, dtype=0)
+    args.update(kw)
+    arr = (ctypes.c_int64 * 12)(*strides)
+    ptr = None if kw.get("null_strides") else ctypes.cast(arr, ctypes.c_void_p)
+    return fa.lib().fa_fwd_strided(args["q"], args["k"], args["v"], args["o"], args["lse"], ptr,
+                                   args["B"], args["H"], args["Hkv"], args["n"], args["d"],
+                                   args["causal"], args["window"],
+                                   ctypes.c_float(args["scale"]), args["dtype"], None)
+
+
+def _bad(i, val):
+    B, H, n, d = 2, 4, 100, 128
+    s = [n * H * d, d, H * d, n * 2 * d, d, 2 * d, n * 2 * d, d, 2 * d, n * H * d, d, H * d]
+    s[i] = val
+    return s
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(o=None), -1), (dict(null_strides=True), -1),
+    (dict(B=0), -2), (dict(H=3, Hkv=2), -2), (dict(causal=5), -2), (dict(scale=0.0), -2),
+    (dict(strides=_bad(2, 64)), -2),         # q row stride < d
+    (dict(strides=_bad(5, 4 * 128)), -2),    # k and v row strides differ
+    (dict(strides=_bad(0, -8)), -2),         # negative
+    (dict(strides=_bad(1, 129)), -2),        # not a multiple of 8
+    (dict(d=96), -3), (dict(dtype=1), -3),
+])
+def test_strided_rejects(lib, kw, status):
+    kw = dict(kw)
+    strides = kw.pop("strides", None)
+    assert _strided(strides, **kw) == status
 
