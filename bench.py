@@ -344,6 +344,46 @@ def time_decode_fp8(fa, torch, np, bf, stream, reps: int = 20):
     return [rec]
 
 
+# The experiment matrix of the xxqk.cn sliding-window prefill article §9.2:
+# sequence length x window (or full attention) x batch, bidirectional band.
+SWEEP = dict(n=(4096, 8192, 16384, 32768), window=(512, 1024, 2048, -1), batch=(1, 2, 4, 8),
+             H=32, Hkv=32, d=128, seed=14)
+
+
+def run_sweep(fa, torch, stream, reps: int = 3):
+    """Time fa_fwd over the sweep; returns one record per (n, window, batch)."""
+    c = SWEEP
+    res = []
+    for n in c["n"]:
+        for B in c["batch"]:
+            g = torch.Generator(device="cuda").manual_seed(c["seed"] + n + B)
+            shp_q, shp_kv = (B, c["H"], n, c["d"]), (B, c["Hkv"], n, c["d"])
+            q = torch.randn(shp_q, generator=g, device="cuda").to(torch.bfloat16)
+            k = torch.randn(shp_kv, generator=g, device="cuda").to(torch.bfloat16)
+            v = torch.randn(shp_kv, generator=g, device="cuda").to(torch.bfloat16)
+            o = torch.empty_like(q)
+            lse = torch.empty((B, c["H"], n), dtype=torch.float32, device="cuda")
+            full_ms = None
+            for w in sorted(c["window"], key=lambda x: x < 0, reverse=True):  # full first
+                ms = _time(torch, stream, lambda: fa.fa_fwd(
+                    q, k, v, o, lse, B, c["H"], c["Hkv"], n, c["d"], 0, w,
+                    1.0 / math.sqrt(c["d"]), fa.FA_BF16, stream), reps)
+                pairs = inband_pairs(n, False, w) * B * c["H"]
+                tf = 4 * c["d"] * pairs / (ms * 1e-3) / 1e12
+                if w < 0:
+                    full_ms = ms
+                rec = {"n": n, "window": w, "batch": B, "ms": round(ms, 4),
+                       "TFLOP/s": round(tf, 2), "speedup_vs_full": round(full_ms / ms, 2),
+                       "pair_ratio_full_over_band": round(inband_pairs(n, False, -1) /
+                                                          inband_pairs(n, False, w), 2)}
+                res.append(rec)
+                log(f"sweep n={n} w={w} B={B}: {ms:.3f} ms {tf:.1f} TFLOP/s "
+                    f"x{rec['speedup_vs_full']} vs full (pairs x{rec['pair_ratio_full_over_band']})")
+            del q, k, v, o, lse
+            torch.cuda.empty_cache()
+    return res
+
+
 def blocksparse_causal_pairs(layout, n: int, block_q: int, block_k: int) -> int:
     """Visible (query, key) pairs of a block layout under a causal mask."""
     import numpy as np
@@ -423,6 +463,9 @@ def main():
                          "(no GPU needed)")
     ap.add_argument("--bwd-steps", type=int, default=5,
                     help="timed fa_bwd calls on the prefill workload (0: skip the backward)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time the length x window x batch matrix of bidirectional band "
+                         "prefill (n 4K-32K, w 512/1024/2048/full, batch 1-8) into 'sweep'")
     ap.add_argument("--all-workloads", action="store_true",
                     help="also time every workload (fp32 n=256, causal n=4096, band n=32768, "
                          "ragged batch, chunked prefill over pages, block-sparse, FP8 decode) "
@@ -575,6 +618,8 @@ def main():
         out["other_workloads"] = (time_other_workloads(fa, torch, np, bf, stream) +
                                   time_ragged_workloads(fa, torch, np, bf, stream) +
                                   time_decode_fp8(fa, torch, np, bf, stream))
+    if args.sweep:
+        out["sweep"] = run_sweep(fa, torch, stream)
     log("timing the oracle on a bounded sample")
     out["cpu_baseline"] = cpu_baseline(pin, max(1, args.cpu_rows),
                                        heads=[0, 5, 10, 15, 16, 21, 26, 31])

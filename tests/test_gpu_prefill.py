@@ -106,3 +106,29 @@ def test_prefill_full_size_sampled(name):
                                    scale, rows=rows)
     compare(o[:, :, rows], lse[:, :, rows], o_ref, lse_ref, TOL_BF16, name)
     assert np.isfinite(o).all() and np.isfinite(lse).all()
+
+
+# Points of the length x window x batch matrix (bidirectional band) the bench
+# sweeps, checked on sampled rows of two heads.
+SWEEP_POINTS = [(4096, 512, 2), (4096, -1, 2), (8192, 1024, 1), (16384, 2048, 1),
+                (32768, 512, 1), (32768, -1, 1)]
+
+
+@pytest.mark.parametrize("n,window,B", SWEEP_POINTS,
+                         ids=[f"n{n}w{w}b{b}" for n, w, b in SWEEP_POINTS])
+def test_sweep_points_sampled(n, window, B):
+    say(f"sweep point n={n} w={window} B={B}")
+    H, d = 32, 128
+    inp = prefill_inputs(B, H, H, n, d, seed=14 + n + B)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = run_prefill(inp, 0, window, scale)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    rows = _sample_rows(n, [0, 1, window - 1, window, window + 1, n // 2, n - 1], seed=n,
+                        count=12)
+    for b in range(B):
+        for h in (0, H - 1):
+            o_ref, lse_ref = attention_fwd(inp["q"][b:b + 1, h:h + 1], inp["k"][b:b + 1, h:h + 1],
+                                           inp["v"][b:b + 1, h:h + 1], False, window, scale,
+                                           rows=rows)
+            compare(o[b:b + 1, h:h + 1, rows], lse[b:b + 1, h:h + 1, rows], o_ref, lse_ref,
+                    TOL_BF16, f"sweep n{n} w{window} b{b} h{h}")
