@@ -35,11 +35,11 @@
 //     registers), double-buffered: the next tile's loads are in flight during
 //     the current tile; one barrier per tile.  Tiles are dense with an XOR
 //     chunk swizzle instead of padding.
-//   * Grid order: heaviest causal query tiles first; inside each round of B*H
-//     tiles, workgroups that share a key/value head are placed on the same XCD
-//     (dispatch is round-robin over the 8 XCDs), so their K/V reads share L2,
-//     and the key/value groups are dealt to the XCDs in turn so every XCD gets
-//     an equal share of every sequence.
+//   * Grid order: key/value groups are dealt to the 8 XCDs in turn (dispatch
+//     is round-robin), and each XCD runs its groups one after another, a
+//     group's query tiles heaviest causal first with its query heads side by
+//     side: the workgroups an XCD runs together read the same K/V tiles from
+//     its L2, and every XCD gets an equal share of every sequence.
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -162,25 +162,32 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a)
   const int BH = a.B * a.H;
 
   // ---- workgroup -> (b, h, query tile) ----
-  const int idx = blockIdx.x;
-  const int round = idx / BH;
-  const int p = idx - round * BH;
-  const int qb = a.causal ? (a.nqb - 1 - round) : round;
-  // Inside a round, workgroup p runs on XCD p % 8 (round-robin dispatch).
-  // Key/value groups (b, g) are dealt to XCDs in turn and a group's G query
-  // heads follow each other on its XCD: they read the same K/V tiles from one
-  // L2, and every XCD gets an equal share of every sequence (ragged batches
-  // stay balanced).
+  // Workgroup p runs on XCD p % 8 (round-robin dispatch).  Key/value groups
+  // (b, g) are dealt to the XCDs in turn; each XCD then works through its
+  // groups one after another, a group's query tiles heaviest (causal) first
+  // with the group's G query heads side by side.  The workgroups an XCD runs
+  // at once thus read the same K/V tiles from its L2, and every XCD gets an
+  // equal share of every sequence (ragged batches stay balanced).
   const int G = a.H / a.Hkv;
-  int b, h, g;
+  const int NQ = a.nqb;
+  const int idx = blockIdx.x;
+  int b, h, g, qb;
   if (((a.B * a.Hkv) & 7) == 0) {
-    const int j = p >> 3;
-    const int u = (p & 7) + 8 * (j / G);  // (b, g) unit
+    const int j = idx >> 3;
+    const int per_group = G * NQ;
+    const int u = (idx & 7) + 8 * (j / per_group);  // (b, g) unit
+    const int rest = j - (j / per_group) * per_group;
+    const int t = rest / G;
     b = u / a.Hkv;
     g = u - b * a.Hkv;
-    h = g * G + (j - (j / G) * G);
+    h = g * G + (rest - t * G);
+    qb = a.causal ? (NQ - 1 - t) : t;
   } else {
-    // fewer than 8 groups per XCD round: consecutive heads per XCD
+    // Fewer than 8 groups per round: rounds of B*H workgroups, one query
+    // tile each (heaviest causal tiles first), consecutive heads per XCD.
+    const int round = idx / BH;
+    const int p = idx - round * BH;
+    qb = a.causal ? (NQ - 1 - round) : round;
     const int bh = (BH & 7) == 0 ? (p & 7) * (BH >> 3) + (p >> 3) : p;
     b = bh / a.H;
     h = bh - b * a.H;
