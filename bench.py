@@ -79,7 +79,8 @@ def measured_traffic(kernel_key: str, src_hash: str):
 
 KERNEL_KEYS = {  # traffic.json key -> (kernel-name fragments, sources)
     "prefill_bf16": (("prefill_bf16_kernel<128, 4, 64, 0>",), ("prefill_bf16.hip", "common.hpp")),
-    "decode": (("decode_split_kernel<128, 4>", "decode_combine_kernel"), ("decode.hip", "common.hpp")),
+    "decode": (("decode_split_kernel<128, 4, false>", "decode_combine_kernel"),
+               ("decode.hip", "common.hpp")),
     "backward": (("bwd_delta_kernel<128>", "bwd_dkdv_kernel<128>", "bwd_dq_kernel<128>"),
                  ("backward.hip", "common.hpp")),
 }

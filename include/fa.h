@@ -204,7 +204,9 @@ int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, flo
  *   lse      [B, H, n] float32, contiguous (as fa_fwd).
  * The head dim is contiguous; k and v must share their row stride; every
  * stride is >= 0, a multiple of 8 elements, and row strides are >= d; base
- * pointers are 16-byte aligned.  Otherwise as fa_fwd (bf16 only).
+ * pointers are 16-byte aligned.  q, k and v may share memory (packed qkv);
+ * o must not overlap them (it is written while other workgroups still read
+ * k and v).  Otherwise as fa_fwd (bf16 only).
  * Errors: FA_ERR_NULL (also strides NULL), FA_ERR_SHAPE (also bad strides),
  * FA_ERR_UNSUPPORTED, FA_ERR_LAUNCH.
  */
