@@ -34,6 +34,11 @@ Recipe (fixed so every consumer sees bit-identical inputs):
     draws come from the same generators as decode, divided by the per-head
     scale (k_scale[g] = (1 + g/16)/8, v_scale[g] = (1 + g/32)/8) and rounded to
     the nearest OCP E4M3 byte (ties to even, clipped to +-448);
+  * score-stress inputs (``stress_inputs``, ``decode_stress``): standard
+    draws (prefill from ``default_rng([seed, 9])``, Q then K then V) shaped
+    before rounding: "rising" sets q[..., 0] = 4 and adds 849 * j / n to
+    k[..., j, 0] (a ramp over key position j), "falling" subtracts that
+    ramp, "large" multiplies q and k by 8, "flat" sets q = 0;
   * bf16 storage: round-to-nearest-even of the float32 draw to bfloat16;
     the returned float32 arrays hold exactly the rounded values;
   * decode: from ``default_rng(seed)``: the sequence lengths (discrete uniform
@@ -67,6 +72,9 @@ __all__ = [
     "decode_lengths_and_table",
     "decode_sequence_kv",
     "decode_inputs",
+    "STRESS_KINDS",
+    "stress_inputs",
+    "decode_stress",
 ]
 
 
@@ -328,3 +336,69 @@ def decode_fp8_inputs(B: int, H: int, Hkv: int, d: int, page_size: int,
     meta.update(kcache8=k8, vcache8=v8, k_scale=ks, v_scale=vs)
     return meta
 
+
+
+STRESS_KINDS = ("rising", "falling", "large", "flat")
+_RAMP = np.float32(849.0)  # q[0] * ramp * scale ~ 300 at the end, for d = 128
+
+
+def _shape_q(kind: str, q: np.ndarray) -> None:
+    """Shape float32 query draws [..., d] in place."""
+    if kind in ("rising", "falling"):
+        q[..., 0] = np.float32(4.0)
+    elif kind == "large":
+        q *= np.float32(8.0)
+    elif kind == "flat":
+        q[...] = 0.0
+    else:
+        raise ValueError(f"unknown stress kind {kind!r}")
+
+
+def _shape_k(kind: str, k: np.ndarray, span: int) -> None:
+    """Shape float32 key draws [..., L, d] in place; key j sits at position j
+    of its sequence and the ramp runs over ``span`` positions."""
+    if kind in ("rising", "falling"):
+        pos = np.arange(k.shape[-2], dtype=np.float32)
+        ramp = (_RAMP * pos / np.float32(span)).astype(np.float32)
+        k[..., 0] += ramp if kind == "rising" else -ramp
+    elif kind == "large":
+        k *= np.float32(8.0)
+
+
+def stress_inputs(kind: str, B: int, H: int, Hkv: int, n: int, d: int, seed: int) -> dict:
+    """Prefill inputs (layout and keys as ``prefill_inputs``, bf16) whose
+    scores stress the running max and the rescaling of the online softmax:
+    rising along the keys (the row max moves tile after tile), falling (the
+    earliest visible key dominates, later ones underflow), large (scores
+    spread over tens of units, rows near one-hot) or flat (all equal)."""
+    rng = np.random.default_rng([seed, 9])
+    x = {name: _draw(rng, (B, heads, n, d), 1.0)
+         for name, heads in (("q", H), ("k", Hkv), ("v", Hkv))}
+    _shape_q(kind, x["q"])
+    _shape_k(kind, x["k"], n)
+    out = {"dtype": "bf16", "seed": seed, "shape": (B, H, Hkv, n, d), "kind": kind}
+    for name in ("q", "k", "v"):
+        out[name], out[name + "_bits"] = bf16_round(x[name])
+    return out
+
+
+def decode_stress(meta: dict, kind: str, span: int) -> dict:
+    """A decode workload (``decode_inputs`` with values) reshaped like
+    ``stress_inputs``: token t of every sequence gets the ramp at position t
+    (over ``span`` positions); q and the key cache are rounded to bf16 again.
+    Returns a new dict; ``meta`` is left as it is."""
+    out = dict(meta)
+    q = np.array(meta["q"], dtype=np.float32)
+    kc = np.array(meta["kcache"], dtype=np.float32)
+    ps = kc.shape[2]
+    _shape_q(kind, q)
+    for b, L in enumerate(meta["seqlens"]):
+        pages = meta["page_table"][b, :(int(L) + ps - 1) // ps]
+        kb = kc[pages].transpose(1, 0, 2, 3)              # [Hkv, pages, ps, d]
+        shp = kb.shape
+        kb = np.ascontiguousarray(kb).reshape(shp[0], shp[1] * ps, shp[3])
+        _shape_k(kind, kb, span)
+        kc[pages] = kb.reshape(shp).transpose(1, 0, 2, 3)
+    out["q"], out["q_bits"] = bf16_round(q)
+    out["kcache"], out["kcache_bits"] = bf16_round(kc)
+    return out

@@ -85,8 +85,10 @@ def rows_seeing(keys, n, causal, window):
     return np.arange(max(int(lo), 0), min(int(hi), n - 1) + 1)
 
 
-def compare_grad(got, ref, bound, label, tol=TOL_BWD):
-    """Check one gradient tensor against the oracle's, with its bound M."""
+def compare_grad(got, ref, bound, label, tol=TOL_BWD, fro=True):
+    """Check one gradient tensor against the oracle's, with its bound M.
+    ``fro=False`` skips the relative Frobenius criterion (for values that are
+    small differences of large terms, where it measures the cancellation)."""
     from tests.bwd_bounds import BOUND_FACTOR
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
@@ -108,6 +110,6 @@ def compare_grad(got, ref, bound, label, tol=TOL_BWD):
     # The Frobenius criterion is statistical (random rounding signs): it is
     # applied to whole gradients, not to a handful of sampled rows, where one
     # row with cancellation dominates it.
-    if got.size // got.shape[-1] >= 256:
+    if fro and got.size // got.shape[-1] >= 256:
         assert rel_fro <= tol["rel_fro"], f"{label}: relative Frobenius error {rel_fro}"
 

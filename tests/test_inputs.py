@@ -63,3 +63,35 @@ def test_decode_cache_places_sequence_pages():
         phys = meta["page_table"][b, :pb]
         assert np.array_equal(meta["kcache_bits"][phys], kb)
         assert np.array_equal(meta["vcache"][phys], vv)
+
+
+def test_stress_inputs_shapes_and_rounding():
+    from io_aware_exact_fa_amd.inputs import STRESS_KINDS, bf16_bits_to_f32, stress_inputs
+    for kind in STRESS_KINDS:
+        a = stress_inputs(kind, 1, 2, 1, 200, 64, seed=5)
+        b = stress_inputs(kind, 1, 2, 1, 200, 64, seed=5)
+        for name in ("q", "k", "v"):
+            assert np.array_equal(a[name + "_bits"], b[name + "_bits"])
+            assert np.array_equal(bf16_bits_to_f32(a[name + "_bits"]), a[name])
+    r = stress_inputs("rising", 1, 2, 1, 200, 64, seed=5)
+    assert np.all(r["q"][..., 0] == 4.0)
+    # the ramp dominates dim 0 of the keys: increasing along the sequence
+    assert np.all(np.diff(r["k"][0, 0, ::20, 0]) > 0)
+    f = stress_inputs("flat", 1, 2, 1, 200, 64, seed=5)
+    assert np.all(f["q"] == 0.0)
+
+
+def test_decode_stress_ramps_by_position():
+    from io_aware_exact_fa_amd.inputs import decode_inputs, decode_stress
+    m = decode_inputs(2, 4, 2, 32, 16, 1, 100, seed=3, seqlens=[50, 100])
+    s = decode_stress(m, "rising", 100)
+    t = m["page_table"]
+    for b, L in enumerate([50, 100]):
+        for tok in (0, L // 2, L - 1):
+            pg, sl = t[b, tok // 16], tok % 16
+            delta = s["kcache"][pg, :, sl, 0] - m["kcache"][pg, :, sl, 0]
+            assert np.allclose(delta, 849.0 * tok / 100, rtol=0, atol=4.0)
+    assert np.all(s["q"][..., 0] == 4.0)
+    # values other than dim 0 of K are untouched
+    assert np.array_equal(s["kcache"][..., 1:], m["kcache"][..., 1:])
+    assert np.array_equal(s["vcache_bits"], m["vcache_bits"])
