@@ -89,8 +89,9 @@ typedef enum {
  * o_i = sum_{j visible} softmax_j(scale * q_i . k_j) v_j.  Every row sees at
  * least key i, so no row is empty.
  *
- * Limits: B, H, Hkv, n >= 1; H % Hkv == 0; d in {64, 128};
- * B*H*n*d < 2^31 elements per tensor; scale finite.
+ * Limits: B, H, Hkv, n >= 1; H % Hkv == 0; d in {64, 128}; n*d < 2^31;
+ * B*H < 2^31 and ceil(n/128)*B*H < 2^31 (workgroups); scale finite.  A
+ * tensor may hold more than 2^31 elements (offsets are 64-bit).
  * dtype FA_BF16: MFMA path; FA_F32: float32 path.
  * Errors: FA_ERR_NULL (q, k, v, o or lse NULL), FA_ERR_SHAPE,
  * FA_ERR_UNSUPPORTED (d not 64/128 or unknown dtype), FA_ERR_LAUNCH.
@@ -120,7 +121,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * clamped into [0, total] and lengths into [0, max_seqlen]; they only keep
  * memory accesses in bounds.
  * Limits: B, H, Hkv, total, max_seqlen >= 1; H % Hkv == 0; d in {64, 128};
- * dtype FA_BF16; H * total * d < 2^31.
+ * dtype FA_BF16; total*d < 2^31 (tensors of H*total*d elements may be
+ * larger: offsets are 64-bit); ceil(max_seqlen/128)*B*H < 2^31.
  * Errors: FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_LAUNCH.
  */
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -156,6 +158,7 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
  * reads page 0; a query that sees no key (chunk longer than its keys) gives
  * o = 0 and lse = -inf.  They only keep memory accesses in bounds.
  * Limits: B, H, Hkv, total_q, max_seqlen_q, num_pages, max_pages >= 1;
+ * total_q*d < 2^31; ceil(max_seqlen_q/128)*B*H < 2^31 (workgroups);
  * H % Hkv == 0; d in {64, 128}; page_size == 16; dtype FA_BF16.
  * Errors: FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_LAUNCH.
  */

@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 
@@ -16,6 +17,12 @@ namespace {
 bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
 
 bool fits_i32(long long x) { return x >= 0 && x < (long long)INT_MAX; }
+
+// Workgroups of a prefill or backward grid: one per 128 query rows of every
+// (batch, head).  The 1-D grid and the kernels' block indices are 32-bit.
+bool grid_ok(long long rows, long long B, long long H) {
+  return fits_i32((rows + 127) / 128 * B * H);
+}
 
 }  // namespace
 
@@ -43,7 +50,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
   if (!scale_ok(scale)) return FA_ERR_SHAPE;
   if (!fits_i32((long long)n * d)) return FA_ERR_SHAPE;
-  if (!fits_i32((long long)B * H)) return FA_ERR_SHAPE;
+  if (!fits_i32((long long)B * H) || !grid_ok(n, B, H)) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   // A window of n or more restricts nothing; clamp so index sums cannot overflow.
   if (window < 0) window = -1;
@@ -67,8 +74,8 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
   if (H % Hkv != 0) return FA_ERR_SHAPE;
   if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
   if (!scale_ok(scale)) return FA_ERR_SHAPE;
-  if (!fits_i32((long long)H * total * d) || !fits_i32((long long)B * H) ||
-      !fits_i32((long long)B + 1))
+  if (!fits_i32((long long)total * d) || !fits_i32((long long)B * H) ||
+      !fits_i32((long long)B + 1) || !grid_ok(std::min(max_seqlen, total), B, H))
     return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
@@ -89,7 +96,8 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* 
   if (H % Hkv != 0) return FA_ERR_SHAPE;
   if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
   if (!scale_ok(scale)) return FA_ERR_SHAPE;
-  if (!fits_i32((long long)n * d) || !fits_i32((long long)B * H)) return FA_ERR_SHAPE;
+  if (!fits_i32((long long)n * d) || !fits_i32((long long)B * H) || !grid_ok(n, B, H))
+    return FA_ERR_SHAPE;
   for (int i = 0; i < 12; ++i)
     if (strides[i] < 0 || strides[i] % 8 != 0) return FA_ERR_SHAPE;
   const long long rs[4] = {strides[2], strides[5], strides[8], strides[11]};
@@ -117,7 +125,8 @@ int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, flo
   if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
   if (!scale_ok(scale)) return FA_ERR_SHAPE;
   if (layout_heads != 1 && layout_heads != H) return FA_ERR_SHAPE;
-  if (!fits_i32((long long)n * d) || !fits_i32((long long)B * H)) return FA_ERR_SHAPE;
+  if (!fits_i32((long long)n * d) || !fits_i32((long long)B * H) || !grid_ok(n, B, H))
+    return FA_ERR_SHAPE;
   if (n > 131072) return FA_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (block_q != 128 || (block_k != 64 && block_k != 128)) return FA_ERR_UNSUPPORTED;
@@ -143,9 +152,9 @@ int fa_fwd_paged(const void* q, const void* kcache, const void* vcache, const in
   if (H % Hkv != 0) return FA_ERR_SHAPE;
   if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
   if (!scale_ok(scale)) return FA_ERR_SHAPE;
-  if (!fits_i32((long long)H * total_q * d) || !fits_i32((long long)B * H) ||
+  if (!fits_i32((long long)total_q * d) || !fits_i32((long long)B * H) ||
       !fits_i32((long long)B * max_pages) || !fits_i32((long long)max_pages * 16) ||
-      !fits_i32((long long)B + 1))
+      !fits_i32((long long)B + 1) || !grid_ok(std::min(max_seqlen_q, total_q), B, H))
     return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (page_size != 16 || dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
@@ -222,7 +231,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
   if (!scale_ok(scale)) return FA_ERR_SHAPE;
   if (!fits_i32((long long)n * d)) return FA_ERR_SHAPE;
-  if (!fits_i32((long long)B * H)) return FA_ERR_SHAPE;
+  if (!fits_i32((long long)B * H) || !grid_ok(n, B, H)) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < fa::bwd_workspace_bytes(B, H, n)) return FA_ERR_WORKSPACE;

@@ -62,6 +62,7 @@ def _fwd(**kw):
     (dict(H=3, Hkv=2), -2), (dict(causal=2), -2), (dict(scale=0.0), -2),
     (dict(scale=-1.0), -2), (dict(scale=float("inf")), -2), (dict(scale=float("nan")), -2),
     (dict(n=1 << 25, d=128), -2),
+    (dict(H=1 << 28, Hkv=1 << 28, n=1024), -2),  # 2^31 workgroups
     (dict(d=96), -3), (dict(d=256), -3), (dict(dtype=7), -3),
 ])
 def test_fwd_rejects(lib, kw, status):
@@ -122,6 +123,7 @@ def _bwd(**kw):
     (dict(B=0), -2), (dict(H=0), -2), (dict(Hkv=0), -2), (dict(n=0), -2), (dict(d=0), -2),
     (dict(H=3, Hkv=2), -2), (dict(causal=2), -2), (dict(scale=0.0), -2),
     (dict(scale=float("nan")), -2), (dict(n=1 << 25, d=128), -2),
+    (dict(B=1 << 10, H=1 << 18, Hkv=1 << 18, n=1024), -2),  # 2^31 workgroups
     (dict(d=96), -3), (dict(dtype=1), -3), (dict(dtype=7), -3),
     (dict(ws=None), -4), (dict(wsb=1 * 2 * 16 * 4 - 1), -4),
 ])
@@ -152,6 +154,7 @@ def _varlen(**kw):
     (dict(B=0), -2), (dict(H=0), -2), (dict(Hkv=0), -2), (dict(total=0), -2),
     (dict(maxs=0), -2), (dict(d=0), -2), (dict(H=3, Hkv=2), -2), (dict(causal=3), -2),
     (dict(scale=0.0), -2), (dict(total=1 << 24, H=8), -2),
+    (dict(B=1 << 20, H=1 << 10, Hkv=1 << 10, total=256, maxs=256), -2),  # 2^31 workgroups
     (dict(d=96), -3), (dict(dtype=1), -3),
 ])
 def test_varlen_rejects(lib, kw, status):
