@@ -11,9 +11,12 @@
 // exp(lse_s - lse), lse = log sum_s exp(lse_s).
 //
 // gfx950 design (HBM bound: every K/V byte is read exactly once):
-//   * One workgroup per (sequence b, key/value head g, split of 32 pages);
-//     its 4 waves take the split's pages round-robin, one page (16 tokens) at
-//     a time, with the next page's loads in flight.  All G = H/Hkv query
+//   * One workgroup per (sequence b, key/value head g, split of up to 96
+//     pages); its 4 waves take the split's pages round-robin, one page (16
+//     tokens) at a time, with the next page's loads in flight.  The loads go
+//     through range-checked buffer descriptors, so the prefetch is issued
+//     unconditionally (empty range past the wave's last page) and the
+//     compiler waits only for the current page's loads.  All G = H/Hkv query
 //     heads of the group are served from the same K/V bytes.
 //   * Scores: v_mfma_f32_16x16x32_bf16, A = the page's 16 tokens x 32 dims
 //     loaded straight from HBM into registers in the A-operand layout, B = the
@@ -83,10 +86,19 @@ constexpr float kDecodeRescaleThreshold = 8.0f;
 // instruction (16 rows x 32 B) spread over all banks in two passes.
 __device__ __forceinline__ int vswz(int r) { return 2 * (r & 7); }
 
+// Range-checked view of one (page, KV head) slab: loads at offsets past
+// nbytes return zeros without touching memory, so a prefetch past the last
+// page can be issued unconditionally with nbytes = 0.  (Unconditional loads
+// let the compiler count the loads in flight; a load under a branch makes it
+// wait for all of them before the current page's work.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const void* base, int nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, 0x00020000);
+}
+
 // 16 bytes per lane from HBM straight into LDS (lane i -> lds + 16*i).
-__device__ __forceinline__ void dma16(const void* src, void* lds) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, unsigned off, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           off, 0, 0, 0);
 }
 
 // Eight E4M3 bytes (little-endian in two words) widened to bf16; exact, as
@@ -187,29 +199,37 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
   };
   // Page i: K into registers (MFMA A layout: token lane%16, dims 32c +
   // 8*(lane/16) .. +8) and V into the LDS buffer vdst by DMA.  An invalid page
-  // id loads page 0 (in bounds) and its tokens are masked.
+  // id loads page 0 (in bounds) and its tokens are masked; a page past the
+  // wave's last one (i >= cnt) loads nothing (zero-sized range).
   auto load_page = [&](int i, PageRegs& r, char* vdst) {
     int phys = phys_of(i);
     if (phys < 0) phys = 0;
     const size_t base = ((size_t)phys * a.Hkv + g) * kPage * D;
     if constexpr (FP8) {
       (void)vdst;
-      const unsigned char* kp = a.kc8 + base;
-      const unsigned char* vp = a.vc8 + base;
+      const int nb = i < cnt ? kPage * D : 0;
+      const __amdgpu_buffer_rsrc_t rk = page_rsrc(a.kc8 + base, nb);
+      const __amdgpu_buffer_rsrc_t rv = page_rsrc(a.vc8 + base, nb);
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        r.k[c] = *reinterpret_cast<const u32x2*>(kp + col * D + 32 * c + 8 * grp);
+        r.k[c] = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_raw_buffer_load_b64(rk, col * D + 32 * c + 8 * grp, 0, 0));
       // the bytes of the 16-byte bf16 slots the V DMA would have moved
 #pragma unroll
-      for (int j = 0; j < 4; ++j) r.v[j] = *reinterpret_cast<const u32x2*>(vp + v_off[j] / 2);
+      for (int j = 0; j < 4; ++j)
+        r.v[j] = __builtin_bit_cast(u32x2,
+                                    __builtin_amdgcn_raw_buffer_load_b64(rv, v_off[j] / 2, 0, 0));
     } else {
-      const __bf16* kp = a.kc + base;
-      const char* vp = reinterpret_cast<const char*>(a.vc + base);
+      const int nb = i < cnt ? PAGE_BYTES : 0;
+      const __amdgpu_buffer_rsrc_t rk = page_rsrc(a.kc + base, nb);
+      const __amdgpu_buffer_rsrc_t rv = page_rsrc(a.vc + base, nb);
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        r.k[c] = *reinterpret_cast<const bf16x8*>(kp + col * D + 32 * c + 8 * grp);
+        r.k[c] = __builtin_bit_cast(
+            bf16x8,
+            __builtin_amdgcn_raw_buffer_load_b128(rk, (col * D + 32 * c + 8 * grp) * 2, 0, 0));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dma16(vp + v_off[j], vdst + 1024 * j);
+      for (int j = 0; j < 4; ++j) dma16(rv, v_off[j], vdst + 1024 * j);
     }
   };
 
@@ -284,17 +304,22 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
     }
   };
 
-  // Two K register sets and two V buffers: page i+1 is in flight while page i
-  // is processed.
+  // Two page register sets and two V buffers: page i+1 is in flight while
+  // page i is processed.  (For FP8 a second page in flight costs the
+  // registers of a third wave per SIMD and measured slower.)
   PageRegs ka, kb;
-  if (cnt > 0) load_page(0, ka, sV0[wave]);
+  load_page(0, ka, sV0[wave]);
   for (int i = 0; i < cnt; i += 2) {
-    if (i + 1 < cnt) load_page(i + 1, kb, sV1[wave]);
+    load_page(i + 1, kb, sV1[wave]);
     process_page(i, ka, sV0[wave]);
     if (i + 1 >= cnt) break;
-    if (i + 2 < cnt) load_page(i + 2, ka, sV0[wave]);
+    load_page(i + 2, ka, sV0[wave]);
     process_page(i + 1, kb, sV1[wave]);
   }
+
+  // The last prefetch (past the wave's pages, zero-sized) may still be in
+  // flight into a V buffer that holds the partial outputs below.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // Row sums: sum the four token groups of each column.  The accumulator
   // needs no cross-lane sum (lanes hold distinct dims).
@@ -419,8 +444,10 @@ int decode_split_pages(int B, int H, int max_seqlen) {
   while (sp > 8 && groups * ((avg_pages + sp - 1) / sp) < 2048) sp = sp > 12 ? sp / 2 : 8;
   return sp;
 }
-// A wave holds the page ids of its share of a split one per lane.
-static_assert(kDecodeWaves * 64 >= 96, "split pages per wave must fit in 64 lanes");
+// A wave holds the page ids of its share of a split one per lane and reads
+// lane cnt (one past its last page) for the final prefetch.
+static_assert((96 + kDecodeWaves - 1) / kDecodeWaves + 1 <= 64,
+              "a wave's pages plus one must fit in 64 lanes");
 
 int decode_max_splits(int B, int H, int max_seqlen) {
   const int sp = decode_split_pages(B, H, max_seqlen);
