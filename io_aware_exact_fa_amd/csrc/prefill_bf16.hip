@@ -111,14 +111,6 @@ __device__ __forceinline__ int swz(int row) {
     return row & 7;
 }
 
-// 16 bytes per lane from HBM straight into LDS through a 64-bit per-lane
-// address (paged tiles gather rows from several pages): lane i's bytes land at
-// lds + 16*i.
-__device__ __forceinline__ void global_load_lds16(const void* src, void* lds) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
-}
-
 // 16 bytes per lane from HBM straight into LDS: lane i's bytes land at
 // lds + 16*i; the source is base + off, read as zero when off >= nbytes
 // (buffer descriptor range check).
@@ -295,21 +287,30 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a)
     st_off[j] = (unsigned)(r * kv_rs * 2 + c * 16);
     st_row[j] = r;
   }
-  // Paged tiles: the four page ids of tile kt (pages past the sequence's
-  // last one repeat it; an id outside [0, num_pages) reads page 0 instead, so
-  // no access leaves the cache whatever the table holds).
-  const int* pt = nullptr;
-  if constexpr (MODE == kPaged) pt = a.page_table + (size_t)b * a.max_pages;
-  const int last_page = (n_k - 1) >> 4;
-  // The loads are issued a tile ahead; the range check happens at the stage
-  // that uses them, so nothing waits for the loads until then.
-  auto page_ids = [&](int kt) {
-    i32x4 id;
+  // Paged tiles: each slot's byte offset inside its 16-row page.
+  unsigned pg_off[IPW];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) id[j] = pt[min(kt * 4 + j, last_page)];
-    return id;
-  };
-  auto stage = [&](int kt, char* tk, char* tv, i32x4 pid) {
+  for (int j = 0; j < IPW; ++j)
+    pg_off[j] = st_off[j] - (unsigned)(st_row[j] & ~15) * (unsigned)RB;
+  // Paged tiles: a 64-key tile spans four 16-token pages and wave w's load
+  // slots fill exactly page w of the tile, so each wave needs one page id per
+  // tile (pages past the sequence's last one repeat it; an id outside
+  // [0, num_pages) reads page 0 instead, so no access leaves the cache
+  // whatever the table holds).
+  static_assert(MODE != kPaged || BC / NW == 16, "one 16-token page per wave and tile");
+  // The table is read-only during the kernel: read through the constant
+  // address space it is a scalar load, counted apart from the K/V DMAs (a
+  // vector load here made the compiler wait for the next tile's DMAs before
+  // the current tile's products).
+  typedef __attribute__((address_space(4))) const int* const_iptr;
+  const_iptr pt = nullptr;
+  if constexpr (MODE == kPaged)
+    pt = (const_iptr)(uintptr_t)(a.page_table + (size_t)b * a.max_pages);
+  const int last_page = (n_k - 1) >> 4;
+  // The load is issued a tile ahead; the range check happens at the stage
+  // that uses it, so nothing waits for it until then.
+  auto page_id = [&](int kt) { return pt[min(kt * 4 + wave_u, last_page)]; };
+  auto stage = [&](int kt, char* tk, char* tv, int pid) {
     const int k0 = kt * BC;
     if constexpr (MODE != kPaged) {
       (void)pid;
@@ -325,20 +326,22 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a)
         buffer_load_lds16(vb, bytes, st_off[j], tv + (wave_u * IPW + j) * 1024);
       }
     } else {
-      // Rows past the last key repeat the last key's row: finite values that
-      // the mask gives zero weight.
+      // This wave's page is read through a scalar descriptor sized to the
+      // page's rows inside the sequence: rows past the last key read as
+      // zeros (finite, and the mask gives them zero weight).  A page past the
+      // sequence (its id repeats the last page) or an id outside [0,
+      // num_pages) (read as page 0) stays in bounds.  Per lane only the
+      // fixed offset inside the page is needed, so no address arithmetic is
+      // repeated per tile.
+      int pg = __builtin_amdgcn_readfirstlane(pid);
+      pg = (pg < 0 || pg >= a.num_pages) ? 0 : pg;
+      const int p0 = min(kt * 4 + wave_u, last_page) * 16;  // first key of the page read
+      const int rows = min(n_k - p0, 16);
+      const size_t base = ((size_t)pg * a.Hkv + g) * 16 * D;
 #pragma unroll
       for (int j = 0; j < IPW; ++j) {
-        const int re = min(k0 + st_row[j], n_k - 1) - k0;
-        const int pj = re >> 4;
-        int pg = pj == 0 ? pid[0] : pj == 1 ? pid[1] : pj == 2 ? pid[2] : pid[3];
-        pg = (pg < 0 || pg >= a.num_pages) ? 0 : pg;
-        const size_t off = (((size_t)pg * a.Hkv + g) * 16 + (re & 15)) * RB +
-                           (st_off[j] - (unsigned)st_row[j] * RB);
-        global_load_lds16(reinterpret_cast<const char*>(a.k) + off,
-                          tk + (wave_u * IPW + j) * 1024);
-        global_load_lds16(reinterpret_cast<const char*>(a.v) + off,
-                          tv + (wave_u * IPW + j) * 1024);
+        buffer_load_lds16(a.k + base, rows * RB, pg_off[j], tk + (wave_u * IPW + j) * 1024);
+        buffer_load_lds16(a.v + base, rows * RB, pg_off[j], tv + (wave_u * IPW + j) * 1024);
       }
     }
   };
@@ -489,33 +492,29 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a)
       return kt_lo + i;
   };
 
-  // Page ids are fetched one tile ahead of their stage (scalar loads).
-  i32x4 pid_next = i32x4{0, 0, 0, 0};
+  // Page ids are fetched one tile ahead of their stage.  The fetch is issued
+  // whether or not that tile exists (its index is clamped to the sequence's
+  // last page): a load under a branch would make the compiler wait for every
+  // load in flight, the next tile's DMA included, before the current tile.
+  int pid_next = 0;
   if (nt > 0) {
-    if constexpr (MODE == kPaged) pid_next = page_ids(kt_lo);
+    if constexpr (MODE == kPaged) pid_next = page_id(kt_lo);
     stage(kt_at(0), sK0, sV0, pid_next);
-    if constexpr (MODE == kPaged)
-      if (1 < nt) pid_next = page_ids(kt_lo + 1);
+    if constexpr (MODE == kPaged) pid_next = page_id(kt_lo + 1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
   // Unrolled by two so that each tile's buffer is a fixed LDS object.
   for (int i = 0; i < nt; i += 2) {
     const int kt = kt_at(i);
-    if (i + 1 < nt) {
-      stage(kt_at(i + 1), sK1, sV1, pid_next);
-      if constexpr (MODE == kPaged)
-        if (i + 2 < nt) pid_next = page_ids(kt + 2);
-    }
+    if (i + 1 < nt) stage(kt_at(i + 1), sK1, sV1, pid_next);
+    if constexpr (MODE == kPaged) pid_next = page_id(kt + 2);
     tile(kt, sK0, sV0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (i + 1 >= nt) break;
-    if (i + 2 < nt) {
-      stage(kt_at(i + 2), sK0, sV0, pid_next);
-      if constexpr (MODE == kPaged)
-        if (i + 3 < nt) pid_next = page_ids(kt + 3);
-    }
+    if (i + 2 < nt) stage(kt_at(i + 2), sK0, sV0, pid_next);
+    if constexpr (MODE == kPaged) pid_next = page_id(kt + 3);
     tile(kt_at(i + 1), sK1, sV1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
