@@ -96,6 +96,8 @@ struct PrefillArgs {
   // kStrided: element strides (batch, head) and row strides
   long long q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;
   int q_ss, kv_ss, o_ss;
+  // 1: each workgroup runs query blocks NQ-1-t and t (causal load balance)
+  int pair;
 };
 
 // LDS tiles are dense (no padding): row r of a tile holds D bf16 values as
@@ -160,31 +162,36 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a)
   // with the group's G query heads side by side.  The workgroups an XCD runs
   // at once thus read the same K/V tiles from its L2, and every XCD gets an
   // equal share of every sequence (ragged batches stay balanced).
+  // With pairing (causal), workgroup t of a head also runs query block t
+  // after block NQ-1-t: every workgroup then has the same number of key
+  // tiles (2*NQ + 2 for full causal), so the grid ends without a tail of
+  // short blocks.
   const int G = a.H / a.Hkv;
   const int NQ = a.nqb;
+  const int NT = a.pair ? (NQ + 1) / 2 : NQ;  // workgroups per (b, h)
   const int idx = blockIdx.x;
-  int b, h, g, qb;
+  int b, h, g, t;
   if (((a.B * a.Hkv) & 7) == 0) {
     const int j = idx >> 3;
-    const int per_group = G * NQ;
+    const int per_group = G * NT;
     const int u = (idx & 7) + 8 * (j / per_group);  // (b, g) unit
     const int rest = j - (j / per_group) * per_group;
-    const int t = rest / G;
+    t = rest / G;
     b = u / a.Hkv;
     g = u - b * a.Hkv;
     h = g * G + (rest - t * G);
-    qb = a.causal ? (NQ - 1 - t) : t;
   } else {
     // Fewer than 8 groups per round: rounds of B*H workgroups, one query
     // tile each (heaviest causal tiles first), consecutive heads per XCD.
-    const int round = idx / BH;
-    const int p = idx - round * BH;
-    qb = a.causal ? (NQ - 1 - round) : round;
+    t = idx / BH;
+    const int p = idx - t * BH;
     const int bh = (BH & 7) == 0 ? (p & 7) * (BH >> 3) + (p >> 3) : p;
     b = bh / a.H;
     h = bh - b * a.H;
     g = h / G;
   }
+  const int qb_first = a.causal ? (NQ - 1 - t) : t;
+  const int qb_second = (a.pair && t != NQ - 1 - t) ? t : -1;
 
   // Rows of this (b, h): n_q queries, n_k keys, query i at position i + qoff
   // among the keys.  Offsets read from memory are clamped so every access
@@ -239,308 +246,313 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a)
     return v < n_k - 1 ? v : n_k - 1;
   };
 
-  const int q0 = qb * BR;
-  if (q0 >= n_q) return;  // past this sequence's rows (ragged batches)
-  const int qlast = min(q0 + BR, n_q) - 1;
-  const int kt_lo = max(lo_of(q0), 0) / BC;
-  const int hi_last = hi_of(qlast);
-  const int kt_hi = hi_last < 0 ? -1 : hi_last / BC;
+  // One query block: its rows' tile loop and epilogue.
+  auto query_block = [&](const int qb) __attribute__((always_inline)) {
+    const int q0 = qb * BR;
+    if (q0 >= n_q) return;  // past this sequence's rows (ragged batches)
+    const int qlast = min(q0 + BR, n_q) - 1;
+    const int kt_lo = max(lo_of(q0), 0) / BC;
+    const int hi_last = hi_of(qlast);
+    const int kt_hi = hi_last < 0 ? -1 : hi_last / BC;
 
-  // ---- this wave's 32 query rows; lane owns row wq0 + l32 ----
-  const int wq0 = q0 + wave * 32;
-  const bool wave_rows = wq0 < n_q;
-  const int wr1 = min(wq0 + 32, n_q) - 1;
-  const int wlo0 = lo_of(wq0), whi0 = hi_of(wq0);
-  const int wlo1 = lo_of(wr1), whi1 = hi_of(wr1);
-  const int row = wq0 + l32;
-  const int rlo = lo_of(row), rhi = hi_of(row);
+    // ---- this wave's 32 query rows; lane owns row wq0 + l32 ----
+    const int wq0 = q0 + wave * 32;
+    const bool wave_rows = wq0 < n_q;
+    const int wr1 = min(wq0 + 32, n_q) - 1;
+    const int wlo0 = lo_of(wq0), whi0 = hi_of(wq0);
+    const int wlo1 = lo_of(wr1), whi1 = hi_of(wr1);
+    const int row = wq0 + l32;
+    const int rlo = lo_of(row), rhi = hi_of(row);
 
-  // Q^T fragments (B operand): query row l32, dims 16*dc + 8*hi .. +8.
-  bf16x8 qf[NDC];
+    // Q^T fragments (B operand): query row l32, dims 16*dc + 8*hi .. +8.
+    bf16x8 qf[NDC];
 #pragma unroll
-  for (int dc = 0; dc < NDC; ++dc)
-    qf[dc] = (row < n_q) ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)row * q_rs + dc * 16 +
-                                                             hi * 8)
-                         : bf16x8{};
+    for (int dc = 0; dc < NDC; ++dc)
+      qf[dc] = (row < n_q) ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)row * q_rs + dc * 16 +
+                                                               hi * 8)
+                           : bf16x8{};
 
-  f32x16 acc[NDB];
+    f32x16 acc[NDB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
-  float m_ref = kNegInf;  // reference max (base-2 scaled units) of this lane's row
-  float l_run = 0.f;      // this lane's share of the row sum (pair with lane ^ 32)
+    for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+    float m_ref = kNegInf;  // reference max (base-2 scaled units) of this lane's row
+    float l_run = 0.f;      // this lane's share of the row sum (pair with lane ^ 32)
 
-  // ---- direct HBM -> LDS staging of one K/V tile ----
-  // Wave instruction j writes 64 consecutive 16-byte slots; slot s holds
-  // physical chunk s % CPR of tile row s / CPR.  Loads are buffer loads whose
-  // descriptor (in scalar registers) starts at the tile and ends at the end of
-  // the sequence: each lane's offset is a fixed register, and rows past the
-  // end of the sequence read as zeros by the hardware range check (those keys
-  // are masked and their zero values contribute nothing).
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  unsigned st_off[IPW];  // byte offset of the slot's chunk in a dense tile
-  int st_row[IPW];       // tile row of the slot
+    // ---- direct HBM -> LDS staging of one K/V tile ----
+    // Wave instruction j writes 64 consecutive 16-byte slots; slot s holds
+    // physical chunk s % CPR of tile row s / CPR.  Loads are buffer loads whose
+    // descriptor (in scalar registers) starts at the tile and ends at the end of
+    // the sequence: each lane's offset is a fixed register, and rows past the
+    // end of the sequence read as zeros by the hardware range check (those keys
+    // are masked and their zero values contribute nothing).
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    unsigned st_off[IPW];  // byte offset of the slot's chunk in a dense tile
+    int st_row[IPW];       // tile row of the slot
 #pragma unroll
-  for (int j = 0; j < IPW; ++j) {
-    const int s = (wave_u * IPW + j) * 64 + lane;
-    const int r = s / CPR;
-    const int c = (s % CPR) ^ swz<D>(r);
-    st_off[j] = (unsigned)(r * kv_rs * 2 + c * 16);
-    st_row[j] = r;
-  }
-  // Paged tiles: each slot's byte offset inside its 16-row page.
-  unsigned pg_off[IPW];
-#pragma unroll
-  for (int j = 0; j < IPW; ++j)
-    pg_off[j] = st_off[j] - (unsigned)(st_row[j] & ~15) * (unsigned)RB;
-  // Paged tiles: a 64-key tile spans four 16-token pages and wave w's load
-  // slots fill exactly page w of the tile, so each wave needs one page id per
-  // tile (pages past the sequence's last one repeat it; an id outside
-  // [0, num_pages) reads page 0 instead, so no access leaves the cache
-  // whatever the table holds).
-  static_assert(MODE != kPaged || BC / NW == 16, "one 16-token page per wave and tile");
-  // The table is read-only during the kernel: read through the constant
-  // address space it is a scalar load, counted apart from the K/V DMAs (a
-  // vector load here made the compiler wait for the next tile's DMAs before
-  // the current tile's products).
-  typedef __attribute__((address_space(4))) const int* const_iptr;
-  const_iptr pt = nullptr;
-  if constexpr (MODE == kPaged)
-    pt = (const_iptr)(uintptr_t)(a.page_table + (size_t)b * a.max_pages);
-  const int last_page = (n_k - 1) >> 4;
-  // The load is issued a tile ahead; the range check happens at the stage
-  // that uses it, so nothing waits for it until then.
-  auto page_id = [&](int kt) { return pt[min(kt * 4 + wave_u, last_page)]; };
-  auto stage = [&](int kt, char* tk, char* tv, int pid) {
-    const int k0 = kt * BC;
-    if constexpr (MODE != kPaged) {
-      (void)pid;
-      // the descriptor ends after the tile's last row inside the sequence:
-      // later rows read as zero (their offsets lie beyond it, as rows are at
-      // least a row apart)
-      const int bytes = (min(n_k - k0, BC) - 1) * kv_rs * 2 + RB;
-      const __bf16* kb = Kh + (size_t)k0 * kv_rs;
-      const __bf16* vb = Vh + (size_t)k0 * kv_rs;
-#pragma unroll
-      for (int j = 0; j < IPW; ++j) {
-        buffer_load_lds16(kb, bytes, st_off[j], tk + (wave_u * IPW + j) * 1024);
-        buffer_load_lds16(vb, bytes, st_off[j], tv + (wave_u * IPW + j) * 1024);
-      }
-    } else {
-      // This wave's page is read through a scalar descriptor sized to the
-      // page's rows inside the sequence: rows past the last key read as
-      // zeros (finite, and the mask gives them zero weight).  A page past the
-      // sequence (its id repeats the last page) or an id outside [0,
-      // num_pages) (read as page 0) stays in bounds.  Per lane only the
-      // fixed offset inside the page is needed, so no address arithmetic is
-      // repeated per tile.
-      int pg = __builtin_amdgcn_readfirstlane(pid);
-      pg = (pg < 0 || pg >= a.num_pages) ? 0 : pg;
-      const int p0 = min(kt * 4 + wave_u, last_page) * 16;  // first key of the page read
-      const int rows = min(n_k - p0, 16);
-      const size_t base = ((size_t)pg * a.Hkv + g) * 16 * D;
-#pragma unroll
-      for (int j = 0; j < IPW; ++j) {
-        buffer_load_lds16(a.k + base, rows * RB, pg_off[j], tk + (wave_u * IPW + j) * 1024);
-        buffer_load_lds16(a.v + base, rows * RB, pg_off[j], tv + (wave_u * IPW + j) * 1024);
-      }
+    for (int j = 0; j < IPW; ++j) {
+      const int s = (wave_u * IPW + j) * 64 + lane;
+      const int r = s / CPR;
+      const int c = (s % CPR) ^ swz<D>(r);
+      st_off[j] = (unsigned)(r * kv_rs * 2 + c * 16);
+      st_row[j] = r;
     }
-  };
-
-  // Per-lane LDS byte offsets of the fragments (tile-relative).
-  // K fragment (kb, dc): row kb*32 + l32, logical chunk 2*dc + hi.
-  // V^T fragment (db, kc, half): 8-byte transposed read; lane supplies row
-  // 16*kc + 8*half + 4*hi + (lane%16)/4 and dims db*32 + 16*((lane/16)%2) + 4*(lane%4).
-  const int krow_sw = swz<D>(l32);
-  const int vrow = 4 * hi + ((lane & 15) >> 2);
-  // swz depends on row bits 0-3: adding 16*kc keeps it, adding 8*half does not.
-  const int vrow_sw[2] = {swz<D>(vrow), swz<D>(vrow + 8)};
-  const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-
-  const float c2 = a.scale_log2;
-
-  // One key tile from LDS (Ks, Vs): S^T = K Q^T, masked online softmax,
-  // O^T += V^T P^T.
-  auto tile = [&](int kt, const char* Ks, const char* Vs) __attribute__((always_inline)) {
-    const int k0 = kt * BC, k1 = k0 + BC - 1;
-    const bool active = wave_rows && !(k1 < wlo0 || k0 > whi1);
-    const bool full = (k0 >= wlo1) && (k1 <= whi0);
-    if (!active) return;
-    // S^T = K Q^T; the K fragments of the next head-dim chunk are read while
-    // the current chunk's MFMAs run.
-    auto kfrag = [&](int dc, int kb) {
-      const int off = (kb * 32 + l32) * RB + (((2 * dc + hi) ^ krow_sw) << 4);
-      return *reinterpret_cast<const bf16x8*>(Ks + off);
+    // Paged tiles: each slot's byte offset inside its 16-row page.
+    unsigned pg_off[IPW];
+#pragma unroll
+    for (int j = 0; j < IPW; ++j)
+      pg_off[j] = st_off[j] - (unsigned)(st_row[j] & ~15) * (unsigned)RB;
+    // Paged tiles: a 64-key tile spans four 16-token pages and wave w's load
+    // slots fill exactly page w of the tile, so each wave needs one page id per
+    // tile (pages past the sequence's last one repeat it; an id outside
+    // [0, num_pages) reads page 0 instead, so no access leaves the cache
+    // whatever the table holds).
+    static_assert(MODE != kPaged || BC / NW == 16, "one 16-token page per wave and tile");
+    // The table is read-only during the kernel: read through the constant
+    // address space it is a scalar load, counted apart from the K/V DMAs (a
+    // vector load here made the compiler wait for the next tile's DMAs before
+    // the current tile's products).
+    typedef __attribute__((address_space(4))) const int* const_iptr;
+    const_iptr pt = nullptr;
+    if constexpr (MODE == kPaged)
+      pt = (const_iptr)(uintptr_t)(a.page_table + (size_t)b * a.max_pages);
+    const int last_page = (n_k - 1) >> 4;
+    // The load is issued a tile ahead; the range check happens at the stage
+    // that uses it, so nothing waits for it until then.
+    auto page_id = [&](int kt) { return pt[min(kt * 4 + wave_u, last_page)]; };
+    auto stage = [&](int kt, char* tk, char* tv, int pid) {
+      const int k0 = kt * BC;
+      if constexpr (MODE != kPaged) {
+        (void)pid;
+        // the descriptor ends after the tile's last row inside the sequence:
+        // later rows read as zero (their offsets lie beyond it, as rows are at
+        // least a row apart)
+        const int bytes = (min(n_k - k0, BC) - 1) * kv_rs * 2 + RB;
+        const __bf16* kb = Kh + (size_t)k0 * kv_rs;
+        const __bf16* vb = Vh + (size_t)k0 * kv_rs;
+#pragma unroll
+        for (int j = 0; j < IPW; ++j) {
+          buffer_load_lds16(kb, bytes, st_off[j], tk + (wave_u * IPW + j) * 1024);
+          buffer_load_lds16(vb, bytes, st_off[j], tv + (wave_u * IPW + j) * 1024);
+        }
+      } else {
+        // This wave's page is read through a scalar descriptor sized to the
+        // page's rows inside the sequence: rows past the last key read as
+        // zeros (finite, and the mask gives them zero weight).  A page past the
+        // sequence (its id repeats the last page) or an id outside [0,
+        // num_pages) (read as page 0) stays in bounds.  Per lane only the
+        // fixed offset inside the page is needed, so no address arithmetic is
+        // repeated per tile.
+        int pg = __builtin_amdgcn_readfirstlane(pid);
+        pg = (pg < 0 || pg >= a.num_pages) ? 0 : pg;
+        const int p0 = min(kt * 4 + wave_u, last_page) * 16;  // first key of the page read
+        const int rows = min(n_k - p0, 16);
+        const size_t base = ((size_t)pg * a.Hkv + g) * 16 * D;
+#pragma unroll
+        for (int j = 0; j < IPW; ++j) {
+          buffer_load_lds16(a.k + base, rows * RB, pg_off[j], tk + (wave_u * IPW + j) * 1024);
+          buffer_load_lds16(a.v + base, rows * RB, pg_off[j], tv + (wave_u * IPW + j) * 1024);
+        }
+      }
     };
-    f32x16 s[NKB];
-    bf16x8 kcur[NKB], knext[NKB];
+
+    // Per-lane LDS byte offsets of the fragments (tile-relative).
+    // K fragment (kb, dc): row kb*32 + l32, logical chunk 2*dc + hi.
+    // V^T fragment (db, kc, half): 8-byte transposed read; lane supplies row
+    // 16*kc + 8*half + 4*hi + (lane%16)/4 and dims db*32 + 16*((lane/16)%2) + 4*(lane%4).
+    const int krow_sw = swz<D>(l32);
+    const int vrow = 4 * hi + ((lane & 15) >> 2);
+    // swz depends on row bits 0-3: adding 16*kc keeps it, adding 8*half does not.
+    const int vrow_sw[2] = {swz<D>(vrow), swz<D>(vrow + 8)};
+    const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+    const float c2 = a.scale_log2;
+
+    // One key tile from LDS (Ks, Vs): S^T = K Q^T, masked online softmax,
+    // O^T += V^T P^T.
+    auto tile = [&](int kt, const char* Ks, const char* Vs) __attribute__((always_inline)) {
+      const int k0 = kt * BC, k1 = k0 + BC - 1;
+      const bool active = wave_rows && !(k1 < wlo0 || k0 > whi1);
+      const bool full = (k0 >= wlo1) && (k1 <= whi0);
+      if (!active) return;
+      // S^T = K Q^T; the K fragments of the next head-dim chunk are read while
+      // the current chunk's MFMAs run.
+      auto kfrag = [&](int dc, int kb) {
+        const int off = (kb * 32 + l32) * RB + (((2 * dc + hi) ^ krow_sw) << 4);
+        return *reinterpret_cast<const bf16x8*>(Ks + off);
+      };
+      f32x16 s[NKB];
+      bf16x8 kcur[NKB], knext[NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      s[kb] = f32x16{};
-      kcur[kb] = kfrag(0, kb);
-    }
-#pragma unroll
-    for (int dc = 0; dc < NDC; ++dc) {
-      if (dc + 1 < NDC) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) knext[kb] = kfrag(dc + 1, kb);
+      for (int kb = 0; kb < NKB; ++kb) {
+        s[kb] = f32x16{};
+        kcur[kb] = kfrag(0, kb);
       }
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) {
+        if (dc + 1 < NDC) {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) knext[kb] = kfrag(dc + 1, kb);
+        }
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur[kb], qf[dc], s[kb], 0, 0, 0);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) kcur[kb] = knext[kb];
+      }
+      if (!full) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            if (key < rlo || key > rhi) s[kb][r] = kNegInf;
+          }
+      }
+      float mx = kNegInf;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur[kb], qf[dc], s[kb], 0, 0, 0);
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) kcur[kb] = knext[kb];
-    }
-    if (!full) {
+        for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[kb][r]);
+      mx = max_xor32(mx) * c2;
+      // Move the reference max only when the row max outgrows it by more than
+      // the threshold (or on the row's first visible key); wave-uniform branch.
+      const bool need = mx > m_ref + kRescaleThreshold;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float alpha = need ? exp2_fast(m_ref - mx) : 1.f;
+        m_ref = need ? mx : m_ref;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+      }
+      // A row with nothing visible yet keeps m_ref = -inf and sees only -inf
+      // scores here; use 0 so exp2(-inf - m) is 0 rather than NaN.
+      const float m_use = (m_ref == kNegInf) ? 0.f : m_ref;
+      bf16x8 pf[NKC];
+      float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (key < rlo || key > rhi) s[kb][r] = kNegInf;
+          const float pv = exp2_fast(__builtin_fmaf(s[kb][r], c2, -m_use));
+          rs += pv;
+          pf[kb * 2 + (r >> 3)][r & 7] = (__bf16)pv;
         }
-    }
-    float mx = kNegInf;
+      l_run += rs;
+      // O^T += V^T P^T.  MFMA k index 8*hi + t stands for key
+      // 16*kc + 8*(t/4) + 4*hi + t%4, the order the S^T accumulator holds.
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+      for (int kc = 0; kc < NKC; ++kc) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[kb][r]);
-    mx = max_xor32(mx) * c2;
-    // Move the reference max only when the row max outgrows it by more than
-    // the threshold (or on the row's first visible key); wave-uniform branch.
-    const bool need = mx > m_ref + kRescaleThreshold;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float alpha = need ? exp2_fast(m_ref - mx) : 1.f;
-      m_ref = need ? mx : m_ref;
-      l_run *= alpha;
+        for (int db = 0; db < NDB; ++db) {
+          bf16x8 vf;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
-    }
-    // A row with nothing visible yet keeps m_ref = -inf and sees only -inf
-    // scores here; use 0 so exp2(-inf - m) is 0 rather than NaN.
-    const float m_use = (m_ref == kNegInf) ? 0.f : m_ref;
-    bf16x8 pf[NKC];
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pv = exp2_fast(__builtin_fmaf(s[kb][r], c2, -m_use));
-        rs += pv;
-        pf[kb * 2 + (r >> 3)][r & 7] = (__bf16)pv;
-      }
-    l_run += rs;
-    // O^T += V^T P^T.  MFMA k index 8*hi + t stands for key
-    // 16*kc + 8*(t/4) + 4*hi + t%4, the order the S^T accumulator holds.
-#pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        bf16x8 vf;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int r = 16 * kc + 8 * half + vrow;
-          const int cbyte = (db * 32 + vcol) * 2;
-          const int off = r * RB + ((((cbyte >> 4) ^ vrow_sw[half]) << 4) | (cbyte & 15));
-          typedef short i16x4 __attribute__((ext_vector_type(4)));
-          const i16x4 t4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(
-                  (__attribute__((address_space(3))) char*)(Vs) + off));
-          const bf16x4 b4 = __builtin_bit_cast(bf16x4, t4);
-          vf[4 * half + 0] = b4[0];
-          vf[4 * half + 1] = b4[1];
-          vf[4 * half + 2] = b4[2];
-          vf[4 * half + 3] = b4[3];
+          for (int half = 0; half < 2; ++half) {
+            const int r = 16 * kc + 8 * half + vrow;
+            const int cbyte = (db * 32 + vcol) * 2;
+            const int off = r * RB + ((((cbyte >> 4) ^ vrow_sw[half]) << 4) | (cbyte & 15));
+            typedef short i16x4 __attribute__((ext_vector_type(4)));
+            const i16x4 t4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4*)(
+                    (__attribute__((address_space(3))) char*)(Vs) + off));
+            const bf16x4 b4 = __builtin_bit_cast(bf16x4, t4);
+            vf[4 * half + 0] = b4[0];
+            vf[4 * half + 1] = b4[1];
+            vf[4 * half + 2] = b4[2];
+            vf[4 * half + 3] = b4[3];
+          }
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kc], acc[db], 0, 0, 0);
         }
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kc], acc[db], 0, 0, 0);
       }
+    };
+
+    // The key tiles visited, in order: kt_lo .. kt_hi, or for a block-sparse
+    // workgroup the kept ones among them, listed in LDS by wave 0 (ballot +
+    // prefix count over 64 tiles at a time).
+    int nt = kt_hi - kt_lo + 1;
+    unsigned short* tiles = nullptr;
+    if constexpr (MODE == kBlockSparse) {
+      __shared__ unsigned short sTiles[kMaxSparseTiles];
+      __shared__ int sCount;
+      tiles = sTiles;
+      const int lh = a.layout_heads == 1 ? 0 : h;
+      const unsigned char* lay =
+          a.layout + ((size_t)lh * a.nqb + qb) * (size_t)a.layout_cols;
+      if (wave_u == 0) {
+        int cnt = 0;
+        for (int c0 = kt_lo; c0 <= kt_hi; c0 += 64) {
+          const int kt = c0 + lane;
+          // every lane reads an entry of its own row (index clamped to kt_hi)
+          const bool on = (lay[min(kt, kt_hi) >> a.tile_shift] != 0) && kt <= kt_hi;
+          const unsigned long long m = __builtin_amdgcn_ballot_w64(on);
+          const int before = __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32),
+                                                       __builtin_amdgcn_mbcnt_lo((unsigned)m, 0));
+          if (on) sTiles[cnt + before] = (unsigned short)kt;
+          cnt += __builtin_popcountll(m);
+        }
+        if (lane == 0) sCount = cnt;
+      }
+      __syncthreads();
+      nt = __builtin_amdgcn_readfirstlane(sCount);
+    }
+    auto kt_at = [&](int i) {
+      if constexpr (MODE == kBlockSparse)
+        return (int)__builtin_amdgcn_readfirstlane(tiles[i]);
+      else
+        return kt_lo + i;
+    };
+
+    // Page ids are fetched one tile ahead of their stage.  The fetch is issued
+    // whether or not that tile exists (its index is clamped to the sequence's
+    // last page): a load under a branch would make the compiler wait for every
+    // load in flight, the next tile's DMA included, before the current tile.
+    int pid_next = 0;
+    if (nt > 0) {
+      if constexpr (MODE == kPaged) pid_next = page_id(kt_lo);
+      stage(kt_at(0), sK0, sV0, pid_next);
+      if constexpr (MODE == kPaged) pid_next = page_id(kt_lo + 1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+    // Unrolled by two so that each tile's buffer is a fixed LDS object.
+    for (int i = 0; i < nt; i += 2) {
+      const int kt = kt_at(i);
+      if (i + 1 < nt) stage(kt_at(i + 1), sK1, sV1, pid_next);
+      if constexpr (MODE == kPaged) pid_next = page_id(kt + 2);
+      tile(kt, sK0, sV0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (i + 1 >= nt) break;
+      if (i + 2 < nt) stage(kt_at(i + 2), sK0, sV0, pid_next);
+      if constexpr (MODE == kPaged) pid_next = page_id(kt + 3);
+      tile(kt_at(i + 1), sK1, sV1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+
+    // ---- epilogue: O = acc / l, lse = ln(2) * (m + log2 l) ----
+    if (!wave_rows) return;
+    const float lt = sum_xor32(l_run);
+    if (row >= n_q) return;
+    // lt = 0 only for a row that sees no key (a chunk longer than its
+    // sequence's keys): o = 0, lse = -inf.
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    __bf16* orow = Oh + (size_t)row * o_rs;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        bf16x4 ov;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ov[j] = (__bf16)(acc[db][4 * g4 + j] * inv);
+        *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * g4 + 4 * hi) = ov;
+      }
+    if (hi == 0) {
+      const float m_use = (m_ref == kNegInf) ? 0.f : m_ref;
+      Lh[row] = lt > 0.f ? (m_use + log2_fast(lt)) * kLn2 : kNegInf;
     }
   };
-
-  // The key tiles visited, in order: kt_lo .. kt_hi, or for a block-sparse
-  // workgroup the kept ones among them, listed in LDS by wave 0 (ballot +
-  // prefix count over 64 tiles at a time).
-  int nt = kt_hi - kt_lo + 1;
-  unsigned short* tiles = nullptr;
-  if constexpr (MODE == kBlockSparse) {
-    __shared__ unsigned short sTiles[kMaxSparseTiles];
-    __shared__ int sCount;
-    tiles = sTiles;
-    const int lh = a.layout_heads == 1 ? 0 : h;
-    const unsigned char* lay =
-        a.layout + ((size_t)lh * a.nqb + qb) * (size_t)a.layout_cols;
-    if (wave_u == 0) {
-      int cnt = 0;
-      for (int c0 = kt_lo; c0 <= kt_hi; c0 += 64) {
-        const int kt = c0 + lane;
-        // every lane reads an entry of its own row (index clamped to kt_hi)
-        const bool on = (lay[min(kt, kt_hi) >> a.tile_shift] != 0) && kt <= kt_hi;
-        const unsigned long long m = __builtin_amdgcn_ballot_w64(on);
-        const int before = __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32),
-                                                     __builtin_amdgcn_mbcnt_lo((unsigned)m, 0));
-        if (on) sTiles[cnt + before] = (unsigned short)kt;
-        cnt += __builtin_popcountll(m);
-      }
-      if (lane == 0) sCount = cnt;
-    }
-    __syncthreads();
-    nt = __builtin_amdgcn_readfirstlane(sCount);
-  }
-  auto kt_at = [&](int i) {
-    if constexpr (MODE == kBlockSparse)
-      return (int)__builtin_amdgcn_readfirstlane(tiles[i]);
-    else
-      return kt_lo + i;
-  };
-
-  // Page ids are fetched one tile ahead of their stage.  The fetch is issued
-  // whether or not that tile exists (its index is clamped to the sequence's
-  // last page): a load under a branch would make the compiler wait for every
-  // load in flight, the next tile's DMA included, before the current tile.
-  int pid_next = 0;
-  if (nt > 0) {
-    if constexpr (MODE == kPaged) pid_next = page_id(kt_lo);
-    stage(kt_at(0), sK0, sV0, pid_next);
-    if constexpr (MODE == kPaged) pid_next = page_id(kt_lo + 1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  }
-  // Unrolled by two so that each tile's buffer is a fixed LDS object.
-  for (int i = 0; i < nt; i += 2) {
-    const int kt = kt_at(i);
-    if (i + 1 < nt) stage(kt_at(i + 1), sK1, sV1, pid_next);
-    if constexpr (MODE == kPaged) pid_next = page_id(kt + 2);
-    tile(kt, sK0, sV0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (i + 1 >= nt) break;
-    if (i + 2 < nt) stage(kt_at(i + 2), sK0, sV0, pid_next);
-    if constexpr (MODE == kPaged) pid_next = page_id(kt + 3);
-    tile(kt_at(i + 1), sK1, sV1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  }
-
-  // ---- epilogue: O = acc / l, lse = ln(2) * (m + log2 l) ----
-  if (!wave_rows) return;
-  const float lt = sum_xor32(l_run);
-  if (row >= n_q) return;
-  // lt = 0 only for a row that sees no key (a chunk longer than its
-  // sequence's keys): o = 0, lse = -inf.
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  __bf16* orow = Oh + (size_t)row * o_rs;
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      bf16x4 ov;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) ov[j] = (__bf16)(acc[db][4 * g4 + j] * inv);
-      *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * g4 + 4 * hi) = ov;
-    }
-  if (hi == 0) {
-    const float m_use = (m_ref == kNegInf) ? 0.f : m_ref;
-    Lh[row] = lt > 0.f ? (m_use + log2_fast(lt)) * kLn2 : kNegInf;
-  }
+  query_block(qb_first);
+  if (qb_second >= 0) query_block(qb_second);
 }
 
 template <int D, int MODE>
@@ -549,7 +561,13 @@ static hipError_t launch_d(const PrefillArgs& a0, int rows, hipStream_t stream) 
   constexpr int BR = NW * 32;
   PrefillArgs a = a0;
   a.nqb = (rows + BR - 1) / BR;
-  const long long grid = (long long)a.nqb * a.B * a.H;
+  // Pair causal query blocks where all sequences share the block count and
+  // the grid is short: below 8192 workgroups (16 rounds of the 512 the part
+  // holds at once) the tail of short blocks costs ~6 % (B4 H16 n4096); above,
+  // heaviest-first order leaves little tail and pairing measured 1 % slower.
+  a.pair = a.causal && (MODE == kDense || MODE == kStrided || MODE == kBlockSparse) &&
+           (long long)a.nqb * a.B * a.H < 8192;
+  const long long grid = (long long)(a.pair ? (a.nqb + 1) / 2 : a.nqb) * a.B * a.H;
   hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, BC, MODE>), dim3((unsigned)grid), dim3(NW * 64),
                      0, stream, a);
   return hipGetLastError();
