@@ -181,8 +181,9 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a)
     g = u - b * a.Hkv;
     h = g * G + (rest - t * G);
   } else {
-    // Fewer than 8 groups per round: rounds of B*H workgroups, one query
-    // tile each (heaviest causal tiles first), consecutive heads per XCD.
+    // B*Hkv not a multiple of 8 (the groups cannot be dealt evenly to the
+    // XCDs): rounds of B*H workgroups, one query tile each (heaviest causal
+    // tiles first), consecutive heads on one XCD when B*H is a multiple of 8.
     t = idx / BH;
     const int p = idx - t * BH;
     const int bh = (BH & 7) == 0 ? (p & 7) * (BH >> 3) + (p >> 3) : p;
