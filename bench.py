@@ -15,7 +15,9 @@ GB/s (bytes of K and V that the sequences' lengths make visible, divided by
 split+merge duration) is reported beside it.  ``cpu_baseline`` times the fp64
 oracle on a bounded sample of the same prefill workload on the host cores.
 ``backward`` times fa_bwd (the gradients) on the same prefill workload after
-the timed steps, outside the step.
+the timed steps, outside the step.  ``roofline.clock`` is the GFX clock the
+part sustains under back-to-back prefill launches (the part is power limited
+there), with the bf16 peak scaled to that clock and the fraction of it.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--bwd-steps N]
 """
@@ -215,6 +217,80 @@ VARLEN = dict(B=16, H=32, Hkv=8, d=128, min_len=1024, max_len=16384, seed=11)
 PAGED = dict(B=16, H=32, Hkv=8, d=128, prefix=(1024, 32768), chunk=(2048, 2048), seed=12)
 BLOCKSPARSE = {"H": 32, "Hkv": 8, "n": 32768, "d": 128, "density": 0.1, "local": 2,
                "global": 1, "seed": 13}
+
+
+def _smi_handle(torch):
+    """The amdsmi handle of cuda:0 (matched by PCI bus id when several GPUs
+    are listed), or None with the reason."""
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        hs = amdsmi.amdsmi_get_processor_handles()
+    except Exception as e:  # library or driver interface missing
+        return None, f"amdsmi unavailable: {e}"
+    if len(hs) == 1:
+        return hs[0], None
+    bus = getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None)
+    for h in hs:
+        try:
+            if bus is not None and int(amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")[1], 16) == bus:
+                return h, None
+        except Exception:
+            pass
+    return None, f"{len(hs)} GPUs listed and none matched cuda:0"
+
+
+def sustained_clock(torch, run, seconds: float, settle: float = 1.0):
+    """Mean GFX clock and socket power while ``run`` is launched back to back.
+
+    The GPU metrics table refreshes about once a second, so the run lasts
+    ``seconds`` and only samples taken after the first ``settle`` seconds are
+    kept.  Returns the mean of the reported current clock (MHz), its per-XCD
+    spread and the mean socket power (W)."""
+    import threading
+    h, why = _smi_handle(torch)
+    if h is None:
+        return {"mhz": None, "why": why}
+    import amdsmi
+    samples, stop = [], threading.Event()
+    t0 = time.perf_counter()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+            except Exception:
+                return
+            if time.perf_counter() - t0 >= settle:
+                samples.append((m.get("current_gfxclk"), m.get("current_gfxclks"),
+                                m.get("current_socket_power")))
+            stop.wait(0.02)
+
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    launched = 0
+    while time.perf_counter() - t0 < seconds:
+        run()
+        launched += 1
+        if launched % 4 == 0:  # keep the queue short so the run ends on time
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    num = lambda x: isinstance(x, (int, float))
+    clk = [c for c, _, _ in samples if num(c)]
+    if not clk:
+        return {"mhz": None, "why": "no clock samples (metrics reported N/A)"}
+    xcds = [[x for x in v if num(x)] for _, v, _ in samples if isinstance(v, list)]
+    xcds = [v for v in xcds if v]
+    pw = [p for _, _, p in samples if num(p)]
+    return {"mhz": round(sum(clk) / len(clk), 1),
+            "xcd_mhz_range": ([min(min(v) for v in xcds), max(max(v) for v in xcds)]
+                              if xcds else None),
+            "socket_power_w": round(sum(pw) / len(pw), 1) if pw else None,
+            "samples": len(clk), "launches": launched,
+            "source": f"amdsmi GPU metrics, current_gfxclk sampled every 20 ms after the "
+                      f"first {settle:g} s of {seconds:g} s of back-to-back launches"}
 
 
 def _time(torch, stream, f, reps):
@@ -467,6 +543,9 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="also time the length x window x batch matrix of bidirectional band "
                          "prefill (n 4K-32K, w 512/1024/2048/full, batch 1-8) into 'sweep'")
+    ap.add_argument("--clock-seconds", type=float, default=2.5,
+                    help="seconds of back-to-back prefill launches after the timed steps while "
+                         "the GFX clock is sampled, for the clock-adjusted peak (0: skip)")
     ap.add_argument("--all-workloads", action="store_true",
                     help="also time every workload (fp32 n=256, causal n=4096, band n=32768, "
                          "ragged batch, chunked prefill over pages, block-sparse, FP8 decode) "
@@ -609,6 +688,16 @@ def main():
                          "kernel": "decode_split_kernel + decode_combine_kernel"},
         },
     }
+    if args.clock_seconds > 0:
+        log(f"sampling the GFX clock over {args.clock_seconds:g} s of prefill launches")
+        clk = sustained_clock(torch, prefill, args.clock_seconds)
+        if clk.get("mhz"):
+            # The published peak assumes the 2400 MHz top clock; at the
+            # sustained clock the same matrix cores deliver proportionally less.
+            at = PEAK_BF16_TFLOPS * clk["mhz"] / 2400.0
+            clk["peak_at_clock"] = round(at, 1)
+            clk["frac_at_clock"] = round(tflops / at, 4)
+        out["roofline"]["clock"] = clk
     del dq, dk, dv
     if args.bwd_steps > 0:
         out["backward"] = time_backward(fa, torch, bf, stream, q, k, v, o, lse, scale,

@@ -1,0 +1,112 @@
+"""Host logic of the benchmark (CPU only): the visible-pair counts that set the
+in-band FLOP numerators, and the clock sampler's filtering of GPU metrics."""
+
+import sys
+import types
+
+import numpy as np
+import pytest
+
+import bench
+
+
+def brute_pairs(n, causal, window):
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    vis = np.ones((n, n), dtype=bool)
+    if causal:
+        vis &= j <= i
+    if window >= 0:
+        vis &= np.abs(i - j) <= window
+    return int(vis.sum())
+
+
+@pytest.mark.parametrize("n", [1, 2, 7, 64, 131])
+@pytest.mark.parametrize("causal", [False, True])
+def test_inband_pairs_matches_explicit_mask(n, causal):
+    for w in sorted({-1, 0, 1, 3, n // 2, n - 2, n - 1, n, n + 5}):
+        if w < -1:
+            continue
+        assert bench.inband_pairs(n, causal, w) == brute_pairs(n, causal, w), (n, causal, w)
+
+
+def test_inband_pairs_workload_sizes():
+    # Causal n = 65536: n(n+1)/2 pairs per head.
+    assert bench.inband_pairs(65536, True, -1) == 65536 * 65537 // 2
+    # Band |i - j| <= 2048 over n = 32768: about 1/8 of n^2 (2w+1 of n per row).
+    p = bench.inband_pairs(32768, False, 2048)
+    assert p == 32768 * 4097 - 2048 * 2049
+    assert 0.12 < p / 32768 ** 2 < 0.126
+
+
+def brute_blocksparse(layout, n, bq, bk):
+    total = 0
+    for lay in layout:
+        vis = np.zeros((n, n), dtype=bool)
+        for a, c in zip(*np.nonzero(lay)):
+            vis[a * bq:(a + 1) * bq, c * bk:(c + 1) * bk] = True
+        vis &= np.tril(np.ones((n, n), dtype=bool))
+        total += int(vis.sum())
+    return total
+
+
+@pytest.mark.parametrize("n", [128, 300, 511])
+def test_blocksparse_pairs_matches_explicit_mask(n):
+    rng = np.random.default_rng(n)
+    bq, bk = 128, 64
+    layout = rng.random((3, -(-n // bq), -(-n // bk))) < 0.4
+    layout[0, :, 0] = True
+    assert bench.blocksparse_causal_pairs(layout, n, bq, bk) == brute_blocksparse(layout, n, bq, bk)
+
+
+class _FakeTorch:
+    class cuda:
+        @staticmethod
+        def synchronize():
+            pass
+
+        @staticmethod
+        def get_device_properties(_):
+            return types.SimpleNamespace(pci_bus_id=3)
+
+
+def _fake_smi(metrics):
+    """An amdsmi stand-in whose metrics table returns successive entries."""
+    it = iter(metrics)
+    last = {}
+
+    def get_metrics(_h):
+        nonlocal last
+        last = next(it, last)
+        return last
+
+    return types.SimpleNamespace(
+        amdsmi_init=lambda: None,
+        amdsmi_get_processor_handles=lambda: ["gpu0"],
+        amdsmi_get_gpu_metrics_info=get_metrics,
+        amdsmi_get_gpu_device_bdf=lambda h: "0000:03:00.0")
+
+
+def test_sustained_clock_averages_settled_samples(monkeypatch):
+    m = {"current_gfxclk": 1800, "current_gfxclks": [1750, 1850], "current_socket_power": 1300}
+    monkeypatch.setitem(sys.modules, "amdsmi", _fake_smi([m] * 10000))
+    r = bench.sustained_clock(_FakeTorch, lambda: None, seconds=0.15, settle=0.05)
+    assert r["mhz"] == 1800
+    assert r["xcd_mhz_range"] == [1750, 1850]
+    assert r["socket_power_w"] == 1300
+    assert r["samples"] >= 1 and r["launches"] >= 1
+
+
+def test_sustained_clock_reports_missing_metrics(monkeypatch):
+    m = {"current_gfxclk": "N/A", "current_gfxclks": "N/A", "current_socket_power": "N/A"}
+    monkeypatch.setitem(sys.modules, "amdsmi", _fake_smi([m] * 10000))
+    r = bench.sustained_clock(_FakeTorch, lambda: None, seconds=0.1, settle=0.0)
+    assert r["mhz"] is None and "N/A" in r["why"]
+
+
+def test_sustained_clock_without_amdsmi(monkeypatch):
+    def boom():
+        raise RuntimeError("no driver")
+    monkeypatch.setitem(sys.modules, "amdsmi", types.SimpleNamespace(amdsmi_init=boom))
+    r = bench.sustained_clock(_FakeTorch, lambda: None, seconds=0.1)
+    assert r["mhz"] is None and "no driver" in r["why"]
