@@ -37,7 +37,8 @@
 //   * FP8 caches (quantised KV, charles2530 blog §9): keys and values are
 //     bytes in the OCP E4M3 format with one scale per KV head.  Every E4M3
 //     value is exact in bf16, so a page's bytes are loaded into registers
-//     one page ahead, widened with v_cvt_pk_f32_fp8 and fed to the same
+//     one page ahead, widened with v_cvt_scalef32_pk_bf16_fp8 (two bytes
+//     per instruction, unit scale) and fed to the same
 //     bf16 MFMAs (V goes through the same LDS buffers, written from
 //     registers); the key scale joins the score scale and the value scale
 //     multiplies the split's output.  Half the bytes of the bf16 cache move.
@@ -103,16 +104,19 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, unsigned off, vo
 
 // Eight E4M3 bytes (little-endian in two words) widened to bf16; exact, as
 // every E4M3 value has at most 4 significant bits and a bf16-range exponent.
+// One v_cvt_scalef32_pk_bf16_fp8 per byte pair, with a unit scale (the
+// per-head scales are applied in fp32 elsewhere), so no rounding occurs.
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(u32x2 w) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   bf16x8 r;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[h], false);
-    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[h], true);
-    r[4 * h + 0] = (__bf16)lo[0];
-    r[4 * h + 1] = (__bf16)lo[1];
-    r[4 * h + 2] = (__bf16)hi[0];
-    r[4 * h + 3] = (__bf16)hi[1];
+    const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[h], 1.0f, false);
+    const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[h], 1.0f, true);
+    r[4 * h + 0] = lo[0];
+    r[4 * h + 1] = lo[1];
+    r[4 * h + 2] = hi[0];
+    r[4 * h + 3] = hi[1];
   }
   return r;
 }
