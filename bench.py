@@ -10,7 +10,8 @@ synthetic input already resident in HBM:
 
 Printed: ONE JSON line.  ``value`` is the prefill's useful (in-band) TFLOP/s:
 4*d FLOPs per visible (query, key) pair, divided by the prefill kernel's
-average duration from HIP events on the stream it runs on.  The decode's KV
+average duration from HIP events on the stream it runs on (the median and the
+range of the per-step durations are printed beside the averages).  The decode's KV
 GB/s (bytes of K and V that the sequences' lengths make visible, divided by
 split+merge duration) is reported beside it.  ``cpu_baseline`` times the fp64
 oracle on a bounded sample of the same prefill workload on the host cores.
@@ -636,8 +637,11 @@ def main():
         e[2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    pre_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    pre_each = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    dec_each = sorted(e[1].elapsed_time(e[2]) for e in evs)
+    pre_ms = sum(pre_each) / args.steps
+    dec_ms = sum(dec_each) / args.steps
+    median = lambda xs: (xs[(len(xs) - 1) // 2] + xs[len(xs) // 2]) / 2
     ms_per_step = wall * 1e3 / args.steps
 
     pairs = inband_pairs(P["n"], bool(P["causal"]), P["window"]) * P["B"] * P["H"]
@@ -674,6 +678,10 @@ def main():
         },
         "prefill_ms": round(pre_ms, 4),
         "decode_ms": round(dec_ms, 4),
+        "prefill_ms_median": round(median(pre_each), 4),
+        "prefill_ms_range": [round(pre_each[0], 4), round(pre_each[-1], 4)],
+        "decode_ms_median": round(median(dec_each), 4),
+        "decode_ms_range": [round(dec_each[0], 4), round(dec_each[-1], 4)],
         "roofline": {
             "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
