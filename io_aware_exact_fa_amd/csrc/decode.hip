@@ -153,13 +153,20 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
   int my_phys = -1;
   if (lane < cnt) my_phys = table[p0 + wave + kDecodeWaves * lane];
 
-  // Query fragments: B operand (32 dims x 16 query columns) per chunk.
+  // Query fragments: B operand (32 dims x 16 query columns) per chunk.  The
+  // contraction's k index may follow any order of the head dims as long as
+  // K and Q agree.  bf16 cache: chunk c, lane group grp holds dims
+  // 32c + 8*grp .. +7.  FP8 cache: chunks 2m and 2m+1 hold dims
+  // 64m + 16*grp .. +7 and .. +15, so a lane's key bytes for both chunks are
+  // one 16-byte load.
   bf16x8 qf[NC];
   {
     const __bf16* qrow = a.q + ((size_t)b * a.H + (size_t)g * G + col) * D;
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-      qf[c] = (col < G) ? *reinterpret_cast<const bf16x8*>(qrow + 32 * c + 8 * grp) : bf16x8{};
+    for (int c = 0; c < NC; ++c) {
+      const int dim0 = FP8 ? 64 * (c >> 1) + 16 * grp + 8 * (c & 1) : 32 * c + 8 * grp;
+      qf[c] = (col < G) ? *reinterpret_cast<const bf16x8*>(qrow + dim0) : bf16x8{};
+    }
   }
 
   // O^T accumulator: 8 blocks of 16 dims x 16 query columns; lane (col q,
@@ -193,8 +200,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
     bf16x8 k[NC];
   };
   struct PageK8 {  // FP8: the page's key and value bytes held by this lane
-    u32x2 k[NC];
-    u32x2 v[4];
+    u32x4 k[NC / 2];  // token col, dims 64m + 16*grp .. +15
+    u32x4 v[2];       // 16-byte piece 64j + lane of the page (row-major)
   };
   using PageRegs = typename std::conditional<FP8, PageK8, PageK>::type;
   auto phys_of = [&](int i) {
@@ -215,14 +222,13 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
       const __amdgpu_buffer_rsrc_t rk = page_rsrc(a.kc8 + base, nb);
       const __amdgpu_buffer_rsrc_t rv = page_rsrc(a.vc8 + base, nb);
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
-        r.k[c] = __builtin_bit_cast(
-            u32x2, __builtin_amdgcn_raw_buffer_load_b64(rk, col * D + 32 * c + 8 * grp, 0, 0));
-      // the bytes of the 16-byte bf16 slots the V DMA would have moved
+      for (int m = 0; m < NC / 2; ++m)
+        r.k[m] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, col * D + 64 * m + 16 * grp, 0, 0));
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        r.v[j] = __builtin_bit_cast(u32x2,
-                                    __builtin_amdgcn_raw_buffer_load_b64(rv, v_off[j] / 2, 0, 0));
+      for (int j = 0; j < 2; ++j)
+        r.v[j] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, 1024 * j + 16 * lane, 0, 0));
     } else {
       const int nb = i < cnt ? PAGE_BYTES : 0;
       const __amdgpu_buffer_rsrc_t rk = page_rsrc(a.kc + base, nb);
@@ -245,14 +251,23 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
 
     bf16x8 kf[NC];
     if constexpr (FP8) {
-      // V: widen and write the page into this wave's buffer, in the layout the
-      // DMA gives the bf16 cache (the reads below follow in program order).
+      // V: widen and write the page into this wave's buffer in the swizzled
+      // layout the DMA gives the bf16 cache (the reads below follow in
+      // program order).  Piece 64j + lane is row r, dims 16k .. +15, i.e.
+      // bf16 chunks 2k and 2k+1, which the swizzle (an XOR with an even
+      // value) keeps side by side.
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<bf16x8*>(const_cast<char*>(vsrc) + 1024 * j + 16 * lane) =
-            e4m3x8_to_bf16(r.v[j]);
+      for (int j = 0; j < 2; ++j) {
+        const int piece = 64 * j + lane, r8 = piece >> 3, k8 = piece & 7;
+        char* dst = const_cast<char*>(vsrc) + r8 * D * 2 + 16 * ((2 * k8) ^ vswz(r8));
+        *reinterpret_cast<bf16x8*>(dst) = e4m3x8_to_bf16(u32x2{r.v[j][0], r.v[j][1]});
+        *reinterpret_cast<bf16x8*>(dst + 16) = e4m3x8_to_bf16(u32x2{r.v[j][2], r.v[j][3]});
+      }
 #pragma unroll
-      for (int c = 0; c < NC; ++c) kf[c] = e4m3x8_to_bf16(r.k[c]);
+      for (int m = 0; m < NC / 2; ++m) {
+        kf[2 * m] = e4m3x8_to_bf16(u32x2{r.k[m][0], r.k[m][1]});
+        kf[2 * m + 1] = e4m3x8_to_bf16(u32x2{r.k[m][2], r.k[m][3]});
+      }
     } else {
 #pragma unroll
       for (int c = 0; c < NC; ++c) kf[c] = r.k[c];
