@@ -30,6 +30,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -58,11 +59,21 @@ def inband_pairs(n: int, causal: bool, window: int) -> int:
     return n * (2 * w + 1) - w * (w + 1)
 
 
+def canonical_source(text: str) -> str:
+    """C++/HIP source with comments removed and whitespace collapsed."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash(*names) -> str:
+    """Key of the recorded HBM counters: a hash of the kernel sources without
+    their comments, so comment edits keep the record valid and code edits
+    void it."""
     h = hashlib.sha256()
     for nm in names:
-        with open(os.path.join(ROOT, "io_aware_exact_fa_amd", "csrc", nm), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "io_aware_exact_fa_amd", "csrc", nm)) as f:
+            h.update(canonical_source(f.read()).encode())
     return h.hexdigest()[:16]
 
 

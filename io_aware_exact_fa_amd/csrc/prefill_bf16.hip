@@ -31,15 +31,19 @@
 //     exceeds it by more than 2^8 (the same reference divides numerator and
 //     denominator, so the result is unchanged); most tiles skip the
 //     accumulator rescale.
-//   * K/V tiles go HBM -> LDS directly (global_load_lds_dwordx4, no staging
-//     registers), double-buffered: the next tile's loads are in flight during
-//     the current tile; one barrier per tile.  Tiles are dense with an XOR
-//     chunk swizzle instead of padding.
+//   * K/V tiles go HBM -> LDS directly (buffer_load_dwordx4 ... lds through
+//     one scalar buffer descriptor per tile, no staging registers; the
+//     descriptor's range check returns zeros past the sequence end),
+//     double-buffered: the next tile's loads are in flight during the current
+//     tile; one barrier per tile.  Tiles are dense with an XOR chunk swizzle
+//     instead of padding.
 //   * Grid order: key/value groups are dealt to the 8 XCDs in turn (dispatch
 //     is round-robin), and each XCD runs its groups one after another, a
 //     group's query tiles heaviest causal first with its query heads side by
 //     side: the workgroups an XCD runs together read the same K/V tiles from
-//     its L2, and every XCD gets an equal share of every sequence.
+//     its L2, and every XCD gets an equal share of every sequence.  Short
+//     causal grids pair query blocks (a workgroup runs block NQ-1-t, then t)
+//     so that every workgroup carries the same number of key tiles.
 
 #include "common.hpp"
 #include "launch.hpp"

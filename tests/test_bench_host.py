@@ -110,3 +110,11 @@ def test_sustained_clock_without_amdsmi(monkeypatch):
     monkeypatch.setitem(sys.modules, "amdsmi", types.SimpleNamespace(amdsmi_init=boom))
     r = bench.sustained_clock(_FakeTorch, lambda: None, seconds=0.1)
     assert r["mhz"] is None and "no driver" in r["why"]
+
+
+def test_source_hash_ignores_comments_only():
+    code = "int f(int a) {\n  return a + 1;  // one more\n}\n"
+    same = "/* header\n   text */\nint f(int a)   {\n  return a + 1;\n}  // done\n"
+    other = "int f(int a) {\n  return a + 2;  // one more\n}\n"
+    assert bench.canonical_source(code) == bench.canonical_source(same)
+    assert bench.canonical_source(code) != bench.canonical_source(other)
