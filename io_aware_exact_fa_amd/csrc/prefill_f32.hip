@@ -4,15 +4,32 @@
 // article §3.1-§3.2 for tiles and the online softmax, §5.1-§5.3 for visiting
 // only key tiles inside the band and masking the straddling ones), kept in
 // float32 end to end: no bf16 rounding anywhere.  Intended for small
-// latency-bound problems; one lane owns one query row.
+// latency-bound problems.
 //
-// Layout: workgroup = one wave of 64 lanes = 64 query rows of one (b, h);
-// key/value tiles of 32 rows staged in LDS and read back as broadcasts.
+// Layout: a workgroup owns 64 query rows of one (b, h); each of its NW waves
+// holds all 64 rows (one lane per row) and takes every NW-th key tile of the
+// band, staged in its own LDS buffer and read back as broadcasts, so the loop
+// needs no workgroup barrier.  Each wave keeps its own running max, sum and
+// accumulator; at the end the NW partial softmaxes are merged through LDS with
+// the rescaling of the online update: weights exp(m_w - M), M the largest
+// partial max (the split-and-merge of the same article's §3.2 algebra that
+// the decode kernel applies across splits).  Splitting the keys over waves
+// cuts the serial chain of a lane NW-fold, which is what bounds these sizes.
 
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace fa {
+
+template <int D>
+struct F32Shape {
+  static constexpr int NW = D == 64 ? 8 : 4;  // waves per workgroup
+  static constexpr int BC = 2048 / D;         // keys per tile: 16 KB of K+V per wave
+  static constexpr int BQ = 64;               // query rows per workgroup
+  static constexpr int STAGE = NW * 2 * BC * D * 4;
+  static constexpr int MERGE = NW * BQ * D * 4;
+  static constexpr int LDS = STAGE > MERGE ? STAGE : MERGE;
+};
 
 struct PrefillF32Args {
   const float* q;
@@ -25,12 +42,16 @@ struct PrefillF32Args {
 };
 
 template <int D>
-__global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillF32Args a) {
-  constexpr int BQ = 64, BC = 32;
-  __shared__ __attribute__((aligned(16))) float Ks[BC * D];
-  __shared__ __attribute__((aligned(16))) float Vs[BC * D];
+__global__ __launch_bounds__(F32Shape<D>::NW * 64) void prefill_f32_kernel(PrefillF32Args a) {
+  using S = F32Shape<D>;
+  constexpr int BQ = S::BQ, BC = S::BC, NW = S::NW;
+  static_assert(S::LDS + 2 * NW * BQ * 4 <= 160 * 1024, "LDS budget");
+  // Staging tiles during the loop, the waves' partial accumulators after it.
+  __shared__ __attribute__((aligned(16))) char smem[S::LDS];
+  __shared__ float sm[NW][BQ], sl[NW][BQ];
 
-  const int lane = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int n = a.n;
   const int qb = blockIdx.x % a.nqb;
   const int bh = blockIdx.x / a.nqb;
@@ -63,10 +84,14 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillF32Args a) {
   }
   float m_run = kNegInf, l_run = 0.f;
   const float c2 = a.scale_log2;
+  float* Ks = reinterpret_cast<float*>(smem) + wave * 2 * BC * D;
+  float* Vs = Ks + BC * D;
 
-  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+  for (int kt = kt_lo + wave; kt <= kt_hi; kt += NW) {
     const int k0 = kt * BC;
-    __syncthreads();
+    // The wave's own buffer: its previous reads precede these writes in the
+    // wave's in-order LDS stream; the fence orders the writes before the reads
+    // of other lanes below.
 #pragma unroll
     for (int i = lane; i < BC * D / 4; i += 64) {
       const int r = i / (D / 4), c = (i - r * (D / 4)) * 4;
@@ -79,7 +104,8 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillF32Args a) {
       *reinterpret_cast<f32x4*>(Ks + r * D + c) = kx;
       *reinterpret_cast<f32x4*>(Vs + r * D + c) = vx;
     }
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
 
     float s[BC];
     float mx = kNegInf;
@@ -124,17 +150,40 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillF32Args a) {
     }
   }
 
-  if (!valid) return;
-  const float inv = 1.f / l_run;
-  float* orow = a.o + ((size_t)(b * a.H + h) * n + row) * D;
+  // ---- merge the waves' partial softmaxes ----
+  sm[wave][lane] = m_run;
+  sl[wave][lane] = l_run;
+  __syncthreads();  // every wave is past its loop: the staging buffers are free
+  float M = kNegInf;
 #pragma unroll
-  for (int d = 0; d < D; d += 4) {
-    f32x4 x;
-    x[0] = acc[d] * inv; x[1] = acc[d + 1] * inv; x[2] = acc[d + 2] * inv; x[3] = acc[d + 3] * inv;
-    *reinterpret_cast<f32x4*>(orow + d) = x;
+  for (int w = 0; w < NW; ++w) M = fmax2(M, sm[w][lane]);
+  const float Mu = (M == kNegInf) ? 0.f : M;
+  float L = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) L = __builtin_fmaf(exp2_fast(sm[w][lane] - Mu), sl[w][lane], L);
+  // Partial accumulators, weighted, as [wave][dim][row]: a lane's stores and
+  // the reads below touch consecutive words across the wave.
+  float* part = reinterpret_cast<float*>(smem);
+  const float wgt = exp2_fast(m_run - Mu);
+#pragma unroll
+  for (int d = 0; d < D; ++d) part[(wave * D + d) * BQ + lane] = acc[d] * wgt;
+  __syncthreads();
+  if (!valid) return;
+  // Wave w finishes dims [w*D/NW, (w+1)*D/NW) of every row.
+  constexpr int DW = D / NW;
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  float* orow = a.o + ((size_t)(b * a.H + h) * n + row) * D + wave * DW;
+#pragma unroll
+  for (int d = 0; d < DW; d += 4) {
+    f32x4 x = f32x4{};
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] += part[(w * D + wave * DW + d + e) * BQ + lane];
+    *reinterpret_cast<f32x4*>(orow + d) = x * inv;
   }
-  const float m_use = (m_run == kNegInf) ? 0.f : m_run;
-  a.lse[(size_t)(b * a.H + h) * n + row] = (m_use + log2_fast(l_run)) * kLn2;
+  if (wave == 0)
+    a.lse[(size_t)(b * a.H + h) * n + row] = L > 0.f ? (Mu + log2_fast(L)) * kLn2 : kNegInf;
 }
 
 hipError_t launch_prefill_f32(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -151,9 +200,11 @@ hipError_t launch_prefill_f32(const void* q, const void* k, const void* v, void*
   a.scale_log2 = scale * kLog2e;
   const long long grid = (long long)a.nqb * B * H;
   if (d == 128)
-    hipLaunchKernelGGL(prefill_f32_kernel<128>, dim3((unsigned)grid), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(prefill_f32_kernel<128>, dim3((unsigned)grid),
+                       dim3(F32Shape<128>::NW * 64), 0, stream, a);
   else if (d == 64)
-    hipLaunchKernelGGL(prefill_f32_kernel<64>, dim3((unsigned)grid), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(prefill_f32_kernel<64>, dim3((unsigned)grid),
+                       dim3(F32Shape<64>::NW * 64), 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

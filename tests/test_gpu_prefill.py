@@ -23,6 +23,13 @@ SMALL = [
     (2, 4, 2, 100, 128, 1, -1, "f32"),
     (1, 2, 1, 77, 64, 0, 10, "f32"),
     (1, 2, 2, 300, 128, 1, 50, "f32"),
+    # The fp32 kernel splits a block's key tiles over its waves: more tiles
+    # than waves, fewer (idle waves), band edges inside a wave's tiles.
+    (1, 1, 1, 1, 64, 0, -1, "f32"),
+    (2, 4, 1, 1000, 64, 1, -1, "f32"),
+    (1, 2, 1, 700, 128, 0, 0, "f32"),
+    (1, 2, 2, 513, 64, 1, 37, "f32"),
+    (1, 2, 1, 1500, 128, 0, 200, "f32"),
     (1, 1, 1, 1, 128, 0, -1, "bf16"),
     (1, 2, 2, 7, 128, 1, -1, "bf16"),
     (1, 2, 1, 256, 128, 0, -1, "bf16"),
