@@ -202,17 +202,7 @@ def time_other_workloads(fa, torch, np, bf, stream, reps: int = 20):
         lse = torch.empty((B, H, n), dtype=torch.float32, device=q.device)
         f = lambda: fa.fa_fwd(q, k, v, o, lse, B, H, Hkv, n, d, causal, window,
                               1.0 / math.sqrt(d), dtype, stream)
-        for _ in range(3):
-            f()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            f()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
+        ms = _time(torch, stream, f, reps)
         flops = 4 * d * inband_pairs(n, bool(causal), window) * B * H
         tf = flops / (ms * 1e-3) / 1e12
         rec = {"workload": name, "ms": round(ms, 4), "TFLOP/s": round(tf, 2)}
@@ -305,10 +295,23 @@ def sustained_clock(torch, run, seconds: float, settle: float = 1.0):
                       f"first {settle:g} s of {seconds:g} s of back-to-back launches"}
 
 
-def _time(torch, stream, f, reps):
-    for _ in range(3):
+def _warm(torch, f, launches: int = 3, seconds: float = 0.5):
+    """At least ``launches`` calls and, after host-side input generation has
+    left the GPU idle, ``seconds`` of back-to-back calls: the clock takes a
+    few hundred milliseconds to ramp (a sub-millisecond kernel timed after 3
+    calls read ~20 % slow)."""
+    t0 = time.perf_counter()
+    done = 0
+    while done < launches or time.perf_counter() - t0 < seconds:
         f()
+        done += 1
+        if done % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+
+
+def _time(torch, stream, f, reps, warm_seconds: float = 0.5):
+    _warm(torch, f, seconds=warm_seconds)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -456,7 +459,7 @@ def run_sweep(fa, torch, stream, reps: int = 3):
             for w in sorted(c["window"], key=lambda x: x < 0, reverse=True):  # full first
                 ms = _time(torch, stream, lambda: fa.fa_fwd(
                     q, k, v, o, lse, B, c["H"], c["Hkv"], n, c["d"], 0, w,
-                    1.0 / math.sqrt(c["d"]), fa.FA_BF16, stream), reps)
+                    1.0 / math.sqrt(c["d"]), fa.FA_BF16, stream), reps, warm_seconds=0.0)
                 pairs = inband_pairs(n, False, w) * B * c["H"]
                 tf = 4 * c["d"] * pairs / (ms * 1e-3) / 1e12
                 if w < 0:
