@@ -18,9 +18,11 @@
 //     unconditionally (empty range past the wave's last page) and the
 //     compiler waits only for the current page's loads.  All G = H/Hkv query
 //     heads of the group are served from the same K/V bytes.
-//   * Scores: v_mfma_f32_16x16x32_bf16, A = the page's 16 tokens x 32 dims
-//     loaded straight from HBM into registers in the A-operand layout, B = the
-//     G query vectors (columns >= G are zero).  Lane l owns query column l%16
+//   * Scores: v_mfma_f32_16x16x32_bf16, A = the page's 16 tokens x 32 dims,
+//     B = the G query vectors (columns >= G are zero).  The bf16 keys are
+//     loaded lane-linearly (whole 128-byte lines per instruction) one page
+//     ahead into registers and pass through a per-wave LDS buffer into the
+//     A-operand layout just before use.  Lane l owns query column l%16
 //     and tokens 4*(l/16) .. +3, so the max / sum over the page's 16 tokens is
 //     4 in-lane values plus two lane swaps (permlane16/32).
 //   * P.V: v_mfma_f32_16x16x16_bf16 over the page's 16 tokens.  Its B operand
@@ -130,6 +132,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
   // Per wave: two V page buffers (double-buffered), filled by LDS DMA.
   __shared__ __attribute__((aligned(1024))) char sV0[kDecodeWaves][PAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char sV1[kDecodeWaves][PAGE_BYTES];
+  // bf16 keys: the page's keys, loaded lane-linearly, pass through this
+  // per-wave buffer on their way into the MFMA operand layout.
+  __shared__ __attribute__((aligned(1024))) char sK[FP8 ? 1 : kDecodeWaves][FP8 ? 16 : PAGE_BYTES];
   __shared__ float Wm[kDecodeWaves][16];
   __shared__ float Wl[kDecodeWaves][16];
   static_assert(GP * D * 4 <= 2 * PAGE_BYTES, "wave partials must fit in its two V buffers");
@@ -233,11 +238,11 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
       const int nb = i < cnt ? PAGE_BYTES : 0;
       const __amdgpu_buffer_rsrc_t rk = page_rsrc(a.kc + base, nb);
       const __amdgpu_buffer_rsrc_t rv = page_rsrc(a.vc + base, nb);
+      static_assert(PAGE_BYTES == NC * 1024, "one 1 KB key piece per register slot");
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
-        r.k[c] = __builtin_bit_cast(
-            bf16x8,
-            __builtin_amdgcn_raw_buffer_load_b128(rk, (col * D + 32 * c + 8 * grp) * 2, 0, 0));
+      for (int j = 0; j < NC; ++j)
+        r.k[j] = __builtin_bit_cast(
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, 1024 * j + 16 * lane, 0, 0));
 #pragma unroll
       for (int j = 0; j < 4; ++j) dma16(rv, v_off[j], vdst + 1024 * j);
     }
@@ -269,8 +274,20 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
         kf[2 * m + 1] = e4m3x8_to_bf16(u32x2{r.k[m][2], r.k[m][3]});
       }
     } else {
+      // Piece j of lane l is row 4j + l/16, 16-byte chunk l%16; it is stored
+      // at chunk (l%16) ^ (row%16) of its row, so that the fragment reads
+      // (16 rows, one chunk each) fall on distinct banks.
+      char* ks = sK[FP8 ? 0 : wave];
 #pragma unroll
-      for (int c = 0; c < NC; ++c) kf[c] = r.k[c];
+      for (int j = 0; j < NC; ++j) {
+        const int kr = 4 * j + (lane >> 4);
+        *reinterpret_cast<bf16x8*>(ks + kr * D * 2 + 16 * ((lane & 15) ^ (kr & 15))) = r.k[j];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        kf[c] = *reinterpret_cast<const bf16x8*>(ks + col * D * 2 + 16 * ((4 * c + grp) ^ (col & 15)));
     }
 
     // S^T = K Q^T: lane (col q, grp) holds tokens 4*grp + rr of query q.
