@@ -13,9 +13,10 @@
 //     the matching key/value tile on chip at a time.
 //
 // gfx950 design (prior art above is NVIDIA-shaped; this is not a translation):
-//   * Workgroup = NW waves of 64 lanes; wave w owns 32 query rows.  Registers
-//     are kept under 256 per lane so two workgroups share a CU: one's softmax
-//     (vector ALU) overlaps the other's matrix-core work.
+//   * Workgroup = NW waves of 64 lanes (8 for dense or strided layouts
+//     without a window, else 4); wave w owns 32 query rows.  Registers are kept under 256 per lane so two waves
+//     share each SIMD (one workgroup of 8 or two of 4 per CU): one wave's
+//     softmax (vector ALU) overlaps the other's matrix-core work.
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 dims (one ds_read_b128 per
 //     lane from LDS), B = Q^T fragment held in VGPRs for the whole loop.  In the
@@ -134,7 +135,7 @@ __device__ __forceinline__ void buffer_load_lds16(const void* base, int nbytes, 
 constexpr float kRescaleThreshold = 8.0f;
 
 template <int D, int NW, int BC, int MODE>
-__global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int BR = NW * 32;         // query rows per workgroup (32 per wave)
   constexpr int RB = D * 2;           // bytes per tile row
   constexpr int CPR = D / 8;          // 16-byte chunks per row
@@ -560,22 +561,39 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a)
   if (qb_second >= 0) query_block(qb_second);
 }
 
-template <int D, int MODE>
-static hipError_t launch_d(const PrefillArgs& a0, int rows, hipStream_t stream) {
-  constexpr int NW = 4, BC = 64;
+template <int D, int MODE, int NW>
+static hipError_t launch_nw(const PrefillArgs& a0, int rows, hipStream_t stream) {
+  constexpr int BC = 64;
   constexpr int BR = NW * 32;
+  constexpr long long kResident = 256 * (8 / NW);  // workgroups the part holds at once
   PrefillArgs a = a0;
   a.nqb = (rows + BR - 1) / BR;
   // Pair causal query blocks where all sequences share the block count and
-  // the grid is short: below 8192 workgroups (16 rounds of the 512 the part
-  // holds at once) the tail of short blocks costs ~6 % (B4 H16 n4096); above,
-  // heaviest-first order leaves little tail and pairing measured 1 % slower.
+  // the grid is short: below 16 rounds of resident workgroups the tail of
+  // short blocks costs ~6 % (B4 H16 n4096); above, heaviest-first order
+  // leaves little tail and pairing measured 1 % slower.
   a.pair = a.causal && (MODE == kDense || MODE == kStrided || MODE == kBlockSparse) &&
-           (long long)a.nqb * a.B * a.H < 8192;
+           (long long)a.nqb * a.B * a.H < 16 * kResident;
   const long long grid = (long long)(a.pair ? (a.nqb + 1) / 2 : a.nqb) * a.B * a.H;
   hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, BC, MODE>), dim3((unsigned)grid), dim3(NW * 64),
                      0, stream, a);
   return hipGetLastError();
+}
+
+// Eight waves (256 query rows, one workgroup per CU) share each staged K/V
+// tile when every row's key range is long (no window: full or causal): half
+// the tile loads and barriers per row, 3 % faster on long causal and full
+// attention.  With a window, four waves (128 rows, two workgroups per CU)
+// leave fewer partly masked tiles at the band edges (8 waves measured 1-5 %
+// slower there).  Ragged batches measured the same either way (each
+// sequence's partly filled last block offsets the gain), chunks over pages
+// keep one 16-token page per wave, and block-sparse layouts are defined over
+// 128-row blocks: four waves for all three.
+template <int D, int MODE>
+static hipError_t launch_d(const PrefillArgs& a, int rows, hipStream_t stream) {
+  if constexpr (MODE == kDense || MODE == kStrided)
+    if (a.window < 0) return launch_nw<D, MODE, 8>(a, rows, stream);
+  return launch_nw<D, MODE, 4>(a, rows, stream);
 }
 
 static PrefillArgs base_args(const void* q, const void* k, const void* v, void* o, float* lse,

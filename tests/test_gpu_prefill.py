@@ -78,6 +78,20 @@ def test_prefill_deterministic():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+@pytest.mark.parametrize("causal", [0, 1], ids=["full", "causal"])
+def test_eight_and_four_wave_workgroups_agree_bitwise(causal):
+    """Without a window the dense forward runs 8-wave workgroups (256 query
+    rows), with a window 4-wave ones (128 rows).  A window of n - 1 leaves the
+    visible set unchanged and each wave visits the same key tiles in the same
+    order either way, so the two launches must agree bit for bit."""
+    n = 1111
+    inp = prefill_inputs(2, 4, 2, n, 128, seed=77 + causal)
+    dev = prefill_device(inp)
+    a = run_prefill(inp, causal, -1, dev=dev)
+    b = run_prefill(inp, causal, n - 1, dev=dev)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
 def _sample_rows(n, extra, seed, count=24):
     rng = np.random.default_rng(seed)
     rows = set(r for r in extra if 0 <= r < n)
