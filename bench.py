@@ -91,11 +91,12 @@ def measured_traffic(kernel_key: str, src_hash: str):
     return rec.get("bytes_per_launch")
 
 
-KERNEL_KEYS = {  # traffic.json key -> (kernel-name fragments, sources)
-    "prefill_bf16": (("prefill_bf16_kernel<128, 4, 64, 0>",), ("prefill_bf16.hip", "common.hpp")),
-    "decode": (("decode_split_kernel<128, 4, false>", "decode_combine_kernel"),
+KERNEL_KEYS = {  # traffic.json key -> (kernel-name patterns, sources)
+    # The dense prefill and the dQ kernel are instantiated per wave count.
+    "prefill_bf16": ((r"prefill_bf16_kernel<128, \d+, 64, 0>",), ("prefill_bf16.hip", "common.hpp")),
+    "decode": ((r"decode_split_kernel<128, 4, false>", r"decode_combine_kernel"),
                ("decode.hip", "common.hpp")),
-    "backward": (("bwd_delta_kernel<128>", "bwd_dkdv_kernel<128>", "bwd_dq_kernel<128>"),
+    "backward": ((r"bwd_delta_kernel<128>", r"bwd_dkdv_kernel<128>", r"bwd_dq_kernel<128(, \d+)?>"),
                  ("backward.hip", "common.hpp")),
 }
 CALIBRATION_COPY_BYTES = 256 << 20
@@ -139,7 +140,8 @@ def traffic_from_counters(fetch_csv: str, write_csv: str) -> dict:
         for counter in ("FETCH_SIZE", "WRITE_SIZE"):
             kib = 0.0
             for frag in frags:
-                hits = [x for name, xs in vals[counter].items() if frag in name for x in xs]
+                hits = [x for name, xs in vals[counter].items() if re.search(frag, name)
+                        for x in xs]
                 if not hits:
                     raise SystemExit(f"{frag} not in the {counter} run")
                 kib += sum(hits) / len(hits)
