@@ -13,8 +13,8 @@
 //     the matching key/value tile on chip at a time.
 //
 // gfx950 design (prior art above is NVIDIA-shaped; this is not a translation):
-//   * Workgroup = NW waves of 64 lanes (8 for dense or strided layouts
-//     without a window, else 4); wave w owns 32 query rows.  Registers are kept under 256 per lane so two waves
+//   * Workgroup = NW waves of 64 lanes (8 for dense or strided layouts whose
+//     rows see 16K keys or more, else 4); wave w owns 32 query rows.  Registers are kept under 256 per lane so two waves
 //     share each SIMD (one workgroup of 8 or two of 4 per CU): one wave's
 //     softmax (vector ALU) overlaps the other's matrix-core work.
 //   * Scores are computed transposed, S^T = K Q^T, with
@@ -581,18 +581,22 @@ static hipError_t launch_nw(const PrefillArgs& a0, int rows, hipStream_t stream)
 }
 
 // Eight waves (256 query rows, one workgroup per CU) share each staged K/V
-// tile when every row's key range is long (no window: full or causal): half
-// the tile loads and barriers per row, 3 % faster on long causal and full
-// attention.  With a window, four waves (128 rows, two workgroups per CU)
-// leave fewer partly masked tiles at the band edges (8 waves measured 1-5 %
-// slower there).  Ragged batches measured the same either way (each
-// sequence's partly filled last block offsets the gain), chunks over pages
-// keep one 16-token page per wave, and block-sparse layouts are defined over
-// 128-row blocks: four waves for all three.
+// tile when every row sees many keys: half the tile loads and barriers per
+// row, 3 % faster on long causal and full attention.  With narrower windows
+// four waves (128 rows, two workgroups per CU) leave fewer partly masked
+// tiles at the band edges; the two tie near 8K keys per row (causal w 4096,
+// band w 4096), 8 waves win from 16K (band w 8192: 2 %, causal w 16384:
+// 0.8 %) and lose below (causal w 1024: 7 %).  Ragged batches measured the
+// same either way (each sequence's partly filled last block offsets the
+// gain), chunks over pages keep one 16-token page per wave, and block-sparse
+// layouts are defined over 128-row blocks: four waves for all three.
 template <int D, int MODE>
 static hipError_t launch_d(const PrefillArgs& a, int rows, hipStream_t stream) {
-  if constexpr (MODE == kDense || MODE == kStrided)
-    if (a.window < 0) return launch_nw<D, MODE, 8>(a, rows, stream);
+  if constexpr (MODE == kDense || MODE == kStrided) {
+    const long long keys_per_row =
+        a.window < 0 ? (1LL << 62) : (a.causal ? a.window + 1LL : 2LL * a.window + 1);
+    if (keys_per_row >= 16384) return launch_nw<D, MODE, 8>(a, rows, stream);
+  }
   return launch_nw<D, MODE, 4>(a, rows, stream);
 }
 

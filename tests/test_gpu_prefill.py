@@ -92,6 +92,27 @@ def test_eight_and_four_wave_workgroups_agree_bitwise(causal):
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+# Windows wide enough for the 8-wave (256-row) workgroups: a band of 8192
+# (16385 keys per row) and a causal window of 16383, with masked band edges
+# inside those workgroups; sampled rows around the edges and the ends.
+WIDE_WINDOWS = [(0, 8192), (1, 16383)]
+
+
+@pytest.mark.parametrize("causal,window", WIDE_WINDOWS,
+                         ids=[f"{'c' if c else 'b'}w{w}" for c, w in WIDE_WINDOWS])
+def test_wide_window_sampled(causal, window):
+    n, H, Hkv, d = 20000, 4, 2, 128
+    say(f"wide window causal={causal} w={window} n={n}")
+    inp = prefill_inputs(1, H, Hkv, n, d, seed=90 + causal)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = run_prefill(inp, causal, window, scale)
+    edges = [0, 1, 255, 256, window - 1, window, window + 1, n - window - 1, n - window,
+             n // 2, n - 257, n - 256, n - 1]
+    rows = _sample_rows(n, edges, seed=window, count=16)
+    o_ref, lse_ref = attention_fwd(inp["q"], inp["k"], inp["v"], causal, window, scale, rows=rows)
+    compare(o[:, :, rows], lse[:, :, rows], o_ref, lse_ref, TOL_BF16, f"wide c{causal} w{window}")
+
+
 def _sample_rows(n, extra, seed, count=24):
     rng = np.random.default_rng(seed)
     rows = set(r for r in extra if 0 <= r < n)
