@@ -545,6 +545,64 @@ def time_backward(fa, torch, bf, stream, q, k, v, o, lse, scale, steps: int):
     }
 
 
+def step_record(steps: int, warmup: int, pre_ms_each, dec_ms_each, wall_s: float,
+                kv_bytes: int, pre_traffic, dec_traffic) -> dict:
+    """The JSON record of the timed steps: per-step prefill and decode
+    durations (ms, HIP events), the wall time of the timed loop (s), the
+    decode's visible K/V bytes, and the measured HBM bytes per launch (or
+    None).  ``value`` and ``roofline.achieved`` use the average prefill
+    duration; medians and ranges are printed beside it."""
+    P, Dc = PREFILL, DECODE
+    pre_each, dec_each = sorted(pre_ms_each), sorted(dec_ms_each)
+    pre_ms = sum(pre_each) / steps
+    dec_ms = sum(dec_each) / steps
+    median = lambda xs: (xs[(len(xs) - 1) // 2] + xs[len(xs) // 2]) / 2
+    pairs = inband_pairs(P["n"], bool(P["causal"]), P["window"]) * P["B"] * P["H"]
+    flops = 4 * P["d"] * pairs
+    tflops = flops / (pre_ms * 1e-3) / 1e12
+    gbs = kv_bytes / (dec_ms * 1e-3) / 1e9
+    return {
+        "metric": "prefill attention TFLOP/s (in-band) & % MFMA peak; decode KV GB/s & % HBM peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(wall_s * 1e3 / steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) draws rounded to bf16)",
+        "config": {
+            "workload": "causal GQA prefill B1 H32/Hkv8 n65536 d128 (draws x0.5) + paged "
+                        "decode B64 H32/Hkv8 d128 L~U[1024,32768] page16",
+            "prefill": {k2: P[k2] for k2 in ("B", "H", "Hkv", "n", "d", "causal", "window")},
+            "decode": {k2: Dc[k2] for k2 in ("B", "H", "Hkv", "d", "page_size", "min_len",
+                                             "max_len")},
+        },
+        "prefill_ms": round(pre_ms, 4),
+        "decode_ms": round(dec_ms, 4),
+        "prefill_ms_median": round(median(pre_each), 4),
+        "prefill_ms_range": [round(pre_each[0], 4), round(pre_each[-1], 4)],
+        "decode_ms_median": round(median(dec_each), 4),
+        "decode_ms_range": [round(dec_each[0], 4), round(dec_each[-1], 4)],
+        "roofline": {
+            "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": pre_traffic, "kernel": "prefill_bf16_kernel",
+            "algorithmic_flops_per_launch": flops,
+        },
+        "decode": {
+            "value": round(gbs, 1), "unit": "GB/s", "kv_bytes": kv_bytes,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": dec_traffic,
+                         "kernel": "decode_split_kernel + decode_combine_kernel"},
+        },
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -653,65 +711,15 @@ def main():
         e[2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    pre_each = sorted(e[0].elapsed_time(e[1]) for e in evs)
-    dec_each = sorted(e[1].elapsed_time(e[2]) for e in evs)
-    pre_ms = sum(pre_each) / args.steps
-    dec_ms = sum(dec_each) / args.steps
-    median = lambda xs: (xs[(len(xs) - 1) // 2] + xs[len(xs) // 2]) / 2
-    ms_per_step = wall * 1e3 / args.steps
-
-    pairs = inband_pairs(P["n"], bool(P["causal"]), P["window"]) * P["B"] * P["H"]
-    flops = 4 * P["d"] * pairs
-    tflops = flops / (pre_ms * 1e-3) / 1e12
     kv_bytes = int(np.sum(din["seqlens"].astype(np.int64))) * Dc["Hkv"] * Dc["d"] * 2 * 2
-    gbs = kv_bytes / (dec_ms * 1e-3) / 1e9
-    log(f"prefill {pre_ms:.3f} ms  {tflops:.1f} TFLOP/s   decode {dec_ms:.3f} ms  {gbs:.0f} GB/s")
-
-    pre_hash = source_hash("prefill_bf16.hip", "common.hpp")
-    dec_hash = source_hash("decode.hip", "common.hpp")
-    pre_traffic = measured_traffic("prefill_bf16", pre_hash)
-    dec_traffic = measured_traffic("decode", dec_hash)
-
-    out = {
-        "metric": "prefill attention TFLOP/s (in-band) & % MFMA peak; decode KV GB/s & % HBM peak",
-        "value": round(tflops, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) draws rounded to bf16)",
-        "config": {
-            "workload": "causal GQA prefill B1 H32/Hkv8 n65536 d128 (draws x0.5) + paged "
-                        "decode B64 H32/Hkv8 d128 L~U[1024,32768] page16",
-            "prefill": {k2: P[k2] for k2 in ("B", "H", "Hkv", "n", "d", "causal", "window")},
-            "decode": {k2: Dc[k2] for k2 in ("B", "H", "Hkv", "d", "page_size", "min_len",
-                                             "max_len")},
-        },
-        "prefill_ms": round(pre_ms, 4),
-        "decode_ms": round(dec_ms, 4),
-        "prefill_ms_median": round(median(pre_each), 4),
-        "prefill_ms_range": [round(pre_each[0], 4), round(pre_each[-1], 4)],
-        "decode_ms_median": round(median(dec_each), 4),
-        "decode_ms_range": [round(dec_each[0], 4), round(dec_each[-1], 4)],
-        "roofline": {
-            "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": pre_traffic, "kernel": "prefill_bf16_kernel",
-            "algorithmic_flops_per_launch": flops,
-        },
-        "decode": {
-            "value": round(gbs, 1), "unit": "GB/s", "kv_bytes": kv_bytes,
-            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": dec_traffic,
-                         "kernel": "decode_split_kernel + decode_combine_kernel"},
-        },
-    }
+    out = step_record(args.steps, args.warmup,
+                      [e[0].elapsed_time(e[1]) for e in evs],
+                      [e[1].elapsed_time(e[2]) for e in evs], wall, kv_bytes,
+                      measured_traffic("prefill_bf16", source_hash("prefill_bf16.hip", "common.hpp")),
+                      measured_traffic("decode", source_hash("decode.hip", "common.hpp")))
+    tflops = out["value"]
+    log(f"prefill {out['prefill_ms']:.3f} ms  {tflops:.1f} TFLOP/s   decode "
+        f"{out['decode_ms']:.3f} ms  {out['decode']['value']:.0f} GB/s")
     if args.clock_seconds > 0:
         log(f"sampling the GFX clock over {args.clock_seconds:g} s of prefill launches")
         clk = sustained_clock(torch, prefill, args.clock_seconds)

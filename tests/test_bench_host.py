@@ -118,3 +118,34 @@ def test_source_hash_ignores_comments_only():
     other = "int f(int a) {\n  return a + 2;  // one more\n}\n"
     assert bench.canonical_source(code) == bench.canonical_source(same)
     assert bench.canonical_source(code) != bench.canonical_source(other)
+
+
+def test_step_record_schema_and_arithmetic():
+    pre = [30.0, 31.0, 29.0, 30.0]
+    dec = [0.74, 0.73, 0.75, 0.74]
+    rec = bench.step_record(4, 3, pre, dec, wall_s=0.124, kv_bytes=4_302_426_112,
+                            pre_traffic=5_500_000_000, dec_traffic=None)
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+                "roofline"):
+        assert key in rec, key
+    assert rec["n_gpus"] == 1 and rec["steps"] == 4 and rec["warmup"] == 3
+    assert rec["higher_is_better"] is True and rec["vs_baseline"] is None
+    assert "workload" in rec["config"] and "model" not in rec["config"]
+    roof = rec["roofline"]
+    for key in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
+        assert key in roof, key
+    # value: in-band FLOPs of the causal n = 65536, H = 32, d = 128 workload
+    # over the average prefill duration (30 ms)
+    flops = 4 * 128 * 32 * 65536 * 65537 // 2
+    assert roof["algorithmic_flops_per_launch"] == flops
+    assert abs(rec["value"] - flops / 30e-3 / 1e12) < 0.01
+    assert roof["achieved"] == rec["value"] and roof["peak"] == 2500.0
+    assert abs(roof["frac"] - rec["value"] / 2500.0) < 1e-4
+    assert roof["traffic"] == 5_500_000_000
+    assert rec["prefill_ms_median"] == 30.0 and rec["prefill_ms_range"] == [29.0, 31.0]
+    assert rec["ms_per_step"] == 31.0
+    dr = rec["decode"]["roofline"]
+    assert dr["bound"] == "hbm" and dr["traffic"] is None
+    assert abs(rec["decode"]["value"] - 4_302_426_112 / 0.74e-3 / 1e9) < 0.1
+    assert abs(dr["frac"] - rec["decode"]["value"] / 8000.0) < 1e-4
