@@ -13,8 +13,9 @@
 //     the matching key/value tile on chip at a time.
 //
 // gfx950 design (prior art above is NVIDIA-shaped; this is not a translation):
-//   * Workgroup = NW waves of 64 lanes (8 for dense or strided layouts whose
-//     rows see 16K keys or more, else 4); wave w owns 32 query rows.  Registers are kept under 256 per lane so two waves
+//   * Workgroup = NW waves of 64 lanes (8 for dense, strided or paged
+//     layouts whose rows see 16K keys or more, else 4); wave w owns 32 query
+//     rows.  Registers are kept under 256 per lane so two waves
 //     share each SIMD (one workgroup of 8 or two of 4 per CU): one wave's
 //     softmax (vector ALU) overlaps the other's matrix-core work.
 //   * Scores are computed transposed, S^T = K Q^T, with
@@ -308,11 +309,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillAr
     for (int j = 0; j < IPW; ++j)
       pg_off[j] = st_off[j] - (unsigned)(st_row[j] & ~15) * (unsigned)RB;
     // Paged tiles: a 64-key tile spans four 16-token pages and wave w's load
-    // slots fill exactly page w of the tile, so each wave needs one page id per
-    // tile (pages past the sequence's last one repeat it; an id outside
+    // slots fill page w of the tile (4 waves) or half of page w/2 (8 waves), so
+    // each wave needs one page id per tile (pages past the sequence's last one repeat it; an id outside
     // [0, num_pages) reads page 0 instead, so no access leaves the cache
     // whatever the table holds).
-    static_assert(MODE != kPaged || BC / NW == 16, "one 16-token page per wave and tile");
+    static_assert(MODE != kPaged || BC / NW == 16 || BC / NW == 8,
+                  "a wave's load slots fill one 16-token page or half of one");
+    constexpr int WPP = MODE == kPaged ? 16 / (BC / NW) : 1;  // waves per page
     // The table is read-only during the kernel: read through the constant
     // address space it is a scalar load, counted apart from the K/V DMAs (a
     // vector load here made the compiler wait for the next tile's DMAs before
@@ -324,7 +327,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillAr
     const int last_page = (n_k - 1) >> 4;
     // The load is issued a tile ahead; the range check happens at the stage
     // that uses it, so nothing waits for it until then.
-    auto page_id = [&](int kt) { return pt[min(kt * 4 + wave_u, last_page)]; };
+    auto page_id = [&](int kt) { return pt[min(kt * 4 + wave_u / WPP, last_page)]; };
     auto stage = [&](int kt, char* tk, char* tv, int pid) {
       const int k0 = kt * BC;
       if constexpr (MODE != kPaged) {
@@ -350,7 +353,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillAr
         // repeated per tile.
         int pg = __builtin_amdgcn_readfirstlane(pid);
         pg = (pg < 0 || pg >= a.num_pages) ? 0 : pg;
-        const int p0 = min(kt * 4 + wave_u, last_page) * 16;  // first key of the page read
+        const int p0 = min(kt * 4 + wave_u / WPP, last_page) * 16;  // first key of the page read
         const int rows = min(n_k - p0, 16);
         const size_t base = ((size_t)pg * a.Hkv + g) * 16 * D;
 #pragma unroll
@@ -586,13 +589,14 @@ static hipError_t launch_nw(const PrefillArgs& a0, int rows, hipStream_t stream)
 // four waves (128 rows, two workgroups per CU) leave fewer partly masked
 // tiles at the band edges; the two tie near 8K keys per row (causal w 4096,
 // band w 4096), 8 waves win from 16K (band w 8192: 2 %, causal w 16384:
-// 0.8 %) and lose below (causal w 1024: 7 %).  Ragged batches measured the
-// same either way (each sequence's partly filled last block offsets the
-// gain), chunks over pages keep one 16-token page per wave, and block-sparse
-// layouts are defined over 128-row blocks: four waves for all three.
+// 0.8 %) and lose below (causal w 1024: 7 %).  Chunks over pages follow the
+// same rule (2 waves per page: 16 chunks of 2048 over long prefixes 2.9 %
+// faster).  Ragged batches measured the same either way (each sequence's
+// partly filled last block offsets the gain) and block-sparse layouts are
+// defined over 128-row blocks: four waves for both.
 template <int D, int MODE>
 static hipError_t launch_d(const PrefillArgs& a, int rows, hipStream_t stream) {
-  if constexpr (MODE == kDense || MODE == kStrided) {
+  if constexpr (MODE == kDense || MODE == kStrided || MODE == kPaged) {
     const long long keys_per_row =
         a.window < 0 ? (1LL << 62) : (a.causal ? a.window + 1LL : 2LL * a.window + 1);
     if (keys_per_row >= 16384) return launch_nw<D, MODE, 8>(a, rows, stream);

@@ -110,6 +110,21 @@ def test_paged_page_permutation_is_bitwise_invariant():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+@pytest.mark.parametrize("causal", [0, 1], ids=["noncausal", "causal"])
+def test_paged_eight_and_four_wave_workgroups_agree_bitwise(causal):
+    """Chunks over pages run 8-wave workgroups (256 query rows, two waves per
+    page) when rows see 16K keys or more (no window) and 4-wave ones (one
+    wave per page) otherwise.  A window of 16000 over sequences shorter than
+    that leaves the visible set unchanged but takes the 4-wave launch; each
+    wave visits the same key tiles in the same order, so the outputs must
+    agree bit for bit."""
+    inp = paged_prefill_inputs(3, 4, 2, 128, 16, 200, 900, 300, 700, seed=4200 + causal)
+    assert int(inp["seqlens_k"].max()) < 16000
+    a = run_paged(inp, causal, -1, 0.09)
+    b = run_paged(inp, causal, 16000, 0.09)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
 # Full-size workloads.
 VARLEN_FULL = dict(B=16, H=32, Hkv=8, d=128, min_len=1024, max_len=16384, seed=11)
 PAGED_FULL = dict(B=16, H=32, Hkv=8, d=128, prefix=(1024, 32768), chunk=(2048, 2048), seed=12)
