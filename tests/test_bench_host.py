@@ -91,8 +91,9 @@ def test_sustained_clock_averages_settled_samples(monkeypatch):
     m = {"current_gfxclk": 1800, "current_gfxclks": [1750, 1850], "current_socket_power": 1300}
     monkeypatch.setitem(sys.modules, "amdsmi", _fake_smi([m] * 10000))
     r = bench.sustained_clock(_FakeTorch, lambda: None, seconds=0.15, settle=0.05)
-    assert r["mhz"] == 1800
+    assert r["mhz"] == 1800 and r["xcd0_mhz"] == 1800
     assert r["xcd_mhz_range"] == [1750, 1850]
+    assert r["xcd_mhz_mean"] == [1750, 1850]
     assert r["socket_power_w"] == 1300
     assert r["samples"] >= 1 and r["launches"] >= 1
 
@@ -149,3 +150,12 @@ def test_step_record_schema_and_arithmetic():
     assert dr["bound"] == "hbm" and dr["traffic"] is None
     assert abs(rec["decode"]["value"] - 4_302_426_112 / 0.74e-3 / 1e9) < 0.1
     assert abs(dr["frac"] - rec["decode"]["value"] / 8000.0) < 1e-4
+
+
+def test_sustained_clock_uses_the_mean_over_xcds(monkeypatch):
+    m = {"current_gfxclk": 1900, "current_gfxclks": [1900, 1700, 2000, 1800],
+         "current_socket_power": 1300}
+    monkeypatch.setitem(sys.modules, "amdsmi", _fake_smi([m] * 10000))
+    r = bench.sustained_clock(_FakeTorch, lambda: None, seconds=0.1, settle=0.0)
+    assert r["mhz"] == 1850 and r["xcd0_mhz"] == 1900
+    assert r["xcd_mhz_mean"] == [1900, 1700, 2000, 1800]
