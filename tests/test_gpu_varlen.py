@@ -75,6 +75,7 @@ PAGED = [
     (3, 2, 1, 64, (10, 500), (5, 130), 1, 50, 6),
     (2, 4, 2, 128, (300, 600), (100, 200), 0, -1, 7),   # chunk sees all keys
     (2, 4, 2, 128, (300, 600), (100, 200), 0, 33, 8),
+    (2, 4, 2, 64, (100, 700), (50, 300), 1, -1, 9),    # d 64, 8-wave workgroups
 ]
 
 
