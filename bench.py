@@ -153,6 +153,18 @@ def traffic_from_counters(fetch_csv: str, write_csv: str) -> dict:
     return out
 
 
+def host_cpu_model() -> str:
+    """The host processor's model name (from /proc/cpuinfo), or 'unknown'."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp, rows_per_head: int, heads: list[int]):
     """The oracle, as it is, on a bounded sample: `rows_per_head` evenly
     spread rows of the given heads of the prefill workload."""
@@ -175,6 +187,7 @@ def cpu_baseline(inp, rows_per_head: int, heads: list[int]):
     inband = sum(int(r) + 1 for r in rows) * len(heads)
     flops = 4 * d * inband
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers,
+            "cpu_model": host_cpu_model(), "cpus_available": len(os.sched_getaffinity(0)),
             "kind": "oracle",
             "sample": f"{rows_per_head} evenly spaced query rows x {len(heads)} heads "
                       f"(KV heads {kv_heads}) of the n=65536 causal prefill, fp64, "

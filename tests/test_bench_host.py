@@ -159,3 +159,8 @@ def test_sustained_clock_uses_the_mean_over_xcds(monkeypatch):
     r = bench.sustained_clock(_FakeTorch, lambda: None, seconds=0.1, settle=0.0)
     assert r["mhz"] == 1850 and r["xcd0_mhz"] == 1900
     assert r["xcd_mhz_mean"] == [1900, 1700, 2000, 1800]
+
+
+def test_host_cpu_model_is_a_string():
+    m = bench.host_cpu_model()
+    assert isinstance(m, str) and m
