@@ -59,6 +59,58 @@ def inband_pairs(n: int, causal: bool, window: int) -> int:
     return n * (2 * w + 1) - w * (w + 1)
 
 
+def tile_schedule(n: int, causal: bool, window: int, B: int = 1, H: int = 1) -> dict:
+    """Host replica of the dense forward's key-tile schedule (fa_fwd, bf16).
+
+    The launch uses workgroups of NW waves (8 when every row sees 16384 keys
+    or more, else 4), each wave owning 32 query rows; key tiles are 64 keys.
+    A workgroup stages the tiles [kt_lo, kt_hi] meeting its rows' band, and a
+    wave computes a staged tile only when one of its rows sees a key in it.
+    Returns, for B*H heads: ``visited_wave_tiles`` ((wave, tile) pairs whose
+    products are computed), ``staged_tiles`` (tiles brought on chip),
+    ``visited_pairs`` (visited_wave_tiles * 32 * 64: the (query, key) pairs
+    the matrix cores evaluate, masked ones included), ``inband_pairs`` and
+    their ratio.  The device counts the same quantities in fa_fwd_tile_count
+    (xxqk.cn sliding-window prefill article §9.1: computed blocks and the
+    KV blocks actually read)."""
+    import numpy as np
+    if window < 0:
+        window = -1
+    window = min(window, n)
+    kpr = (1 << 62) if window < 0 else (window + 1 if causal else 2 * window + 1)
+    nw = 8 if kpr >= 16384 else 4
+    br, bc = 32 * nw, 64
+
+    def lo(i):
+        return i - window if window >= 0 else np.zeros_like(i)
+
+    def hi(i):
+        h = i if causal else (i + window if window >= 0 else np.full_like(i, n - 1))
+        return np.minimum(h, n - 1)
+
+    q0 = np.arange(0, n, br, dtype=np.int64)               # workgroup first rows
+    qlast = np.minimum(q0 + br, n) - 1
+    kt_lo = np.maximum(lo(q0), 0) // bc
+    kt_hi = hi(qlast) // bc
+    staged = int(np.maximum(kt_hi - kt_lo + 1, 0).sum())
+    wq0 = (q0[:, None] + 32 * np.arange(nw)[None, :]).ravel()   # wave first rows
+    tlo = np.repeat(kt_lo, nw)
+    thi = np.repeat(kt_hi, nw)
+    ok = wq0 < n
+    wq0 = wq0[ok]
+    wr1 = np.minimum(wq0 + 32, n) - 1
+    # active tile kt: kt*64 + 63 >= lo(first row) and kt*64 <= hi(last row)
+    a_lo = np.maximum(tlo[ok], -(-(lo(wq0) - (bc - 1)) // bc))
+    a_hi = np.minimum(thi[ok], hi(wr1) // bc)
+    visited = int(np.maximum(a_hi - a_lo + 1, 0).sum())
+    inband = inband_pairs(n, causal, window)
+    heads = B * H
+    return {"waves_per_workgroup": nw, "visited_wave_tiles": visited * heads,
+            "staged_tiles": staged * heads, "visited_pairs": visited * heads * 32 * bc,
+            "inband_pairs": inband * heads,
+            "inband_over_visited": round(inband / (visited * 32 * bc), 6)}
+
+
 def canonical_source(text: str) -> str:
     """C++/HIP source with comments removed and whitespace collapsed."""
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -167,7 +219,11 @@ def host_cpu_model() -> str:
 
 def cpu_baseline(inp, rows_per_head: int, heads: list[int]):
     """The oracle, as it is, on a bounded sample: `rows_per_head` evenly
-    spread rows of the given heads of the prefill workload."""
+    spread rows of the given heads of the prefill workload.  Returns the
+    record and the oracle's outputs for those rows (o [1, heads, R, d], lse
+    [1, heads, R]) with the row indices, for the consistency check.  Runs
+    before the GPU is touched: its worker processes are forked from a process
+    with no GPU state."""
     import numpy as np
     from oracle import attention_fwd
     from oracle.attention import default_workers
@@ -182,16 +238,83 @@ def cpu_baseline(inp, rows_per_head: int, heads: list[int]):
     k = inp["k"][:, [h // group for h in heads]]
     v = inp["v"][:, [h // group for h in heads]]
     t0 = time.perf_counter()
-    attention_fwd(q, k, v, True, -1, 1.0 / math.sqrt(d), rows=rows, workers=workers)
+    o_ref, lse_ref = attention_fwd(q, k, v, True, -1, 1.0 / math.sqrt(d), rows=rows,
+                                   workers=workers)
     dt = time.perf_counter() - t0
     inband = sum(int(r) + 1 for r in rows) * len(heads)
     flops = 4 * d * inband
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers,
-            "cpu_model": host_cpu_model(), "cpus_available": len(os.sched_getaffinity(0)),
-            "kind": "oracle",
-            "sample": f"{rows_per_head} evenly spaced query rows x {len(heads)} heads "
-                      f"(KV heads {kv_heads}) of the n=65536 causal prefill, fp64, "
-                      f"{dt:.1f} s wall; in-band FLOPs of those rows only"}
+    rec = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers,
+           "cpu_model": host_cpu_model(), "cpus_available": len(os.sched_getaffinity(0)),
+           "kind": "oracle",
+           "sample": f"{rows_per_head} evenly spaced query rows x {len(heads)} heads "
+                     f"(KV heads {kv_heads}) of the n=65536 causal prefill, fp64, "
+                     f"{dt:.1f} s wall; in-band FLOPs of those rows only"}
+    return rec, (rows, heads, o_ref, lse_ref)
+
+
+# Tolerances of the parity gate against the fp64 oracle (bf16 I/O with fp32
+# accumulation; float32 throughout), the same as the test suite's.
+TOL = {"bf16": {"max_abs": 2e-2, "mean_abs": 2e-3, "lse": 1e-3},
+       "f32": {"max_abs": 1e-4, "mean_abs": 1e-4, "lse": 1e-3}}
+
+
+def consistency(o, lse, o_ref, lse_ref, dtype: str, what: str) -> dict:
+    """max / mean |dO| and max |d lse| of a sample against the oracle, and
+    whether they pass the parity tolerances (xxqk.cn sliding-window prefill
+    article §8.3 compares the two outputs by their largest absolute error;
+    §9.2 records whether the consistency check passed)."""
+    import numpy as np
+    o = np.asarray(o, dtype=np.float64)
+    lse = np.asarray(lse, dtype=np.float64)
+    d = np.abs(o - o_ref)
+    dl = np.abs(lse - lse_ref)
+    tol = TOL[dtype]
+    rec = {"sample": what, "max_abs": float(d.max()), "mean_abs": float(d.mean()),
+           "lse_max_abs": float(dl.max()), "finite": bool(np.isfinite(o).all() and
+                                                         np.isfinite(lse).all())}
+    rec["pass"] = bool(rec["finite"] and rec["max_abs"] <= tol["max_abs"] and
+                       rec["mean_abs"] <= tol["mean_abs"] and rec["lse_max_abs"] <= tol["lse"])
+    return {k2: (float(f"{x:.4g}") if isinstance(x, float) else x) for k2, x in rec.items()}
+
+
+def decode_oracle_sample(din, seqs, scale):
+    """The decode oracle for the sequences ``seqs`` of a decode workload held
+    as bf16 bits: each sequence's own pages are widened and passed with an
+    identity table.  Returns (o [len(seqs), H, d], lse [len(seqs), H])."""
+    import numpy as np
+    from oracle import decode_fwd
+    from io_aware_exact_fa_amd.inputs import bf16_bits_to_f32
+    ps = din["page_size"]
+    outs, lses = [], []
+    for b in seqs:
+        L = int(din["seqlens"][b])
+        pb = (L + ps - 1) // ps
+        phys = din["page_table"][b, :pb]
+        ob, lb = decode_fwd(din["q"][b:b + 1], bf16_bits_to_f32(din["kcache_bits"][phys]),
+                            bf16_bits_to_f32(din["vcache_bits"][phys]),
+                            np.arange(pb, dtype=np.int32)[None, :], din["seqlens"][b:b + 1],
+                            scale)
+        outs.append(ob[0])
+        lses.append(lb[0])
+    return np.stack(outs), np.stack(lses)
+
+
+def decode_sample_seqs(seqlens, count: int = 8):
+    """Shortest, longest and evenly spread sequences of a decode batch."""
+    import numpy as np
+    B = len(seqlens)
+    pick = {int(np.argmin(seqlens)), int(np.argmax(seqlens))}
+    pick.update(int(x) for x in np.linspace(0, B - 1, count - 2).round())
+    return sorted(pick)
+
+
+def stratified_rows(n: int, block: int, seed: int):
+    """One seeded row of every ``block``-row block of [0, n), plus the ends."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    starts = np.arange(0, n, block)
+    rows = set((starts + rng.integers(0, block, size=starts.size)).tolist()) | {0, n - 1}
+    return np.array(sorted(r for r in rows if r < n))
 
 
 OTHER_WORKLOADS = [  # name, B, H, Hkv, n, d, causal, window, dtype, seed
@@ -201,8 +324,36 @@ OTHER_WORKLOADS = [  # name, B, H, Hkv, n, d, causal, window, dtype, seed
 ]
 
 
+def dense_consistency(torch, inp_or_dev, o, lse, causal, window, scale, dtype, picks,
+                      rows, rows_block: int = 256):
+    """Consistency of a dense prefill output on the (batch, head) pairs
+    ``picks`` and query ``rows``, against the oracle run serially on the
+    host.  ``inp_or_dev`` holds q, k, v as numpy arrays ("q", "k", "v") or
+    device tensors (copied back per head)."""
+    import numpy as np
+    from oracle import attention_fwd
+    H, Hkv = o.shape[1], (inp_or_dev["k"].shape[1])
+    G = H // Hkv
+    rows_t = torch.from_numpy(rows).to(o.device)
+    got_o, got_l, ref_o, ref_l = [], [], [], []
+    for b, h in picks:
+        g = h // G
+        sel = [inp_or_dev[x][b:b + 1, hh:hh + 1] for x, hh in (("q", h), ("k", g), ("v", g))]
+        if not isinstance(sel[0], np.ndarray):
+            sel = [t.float().cpu().numpy() for t in sel]
+        ro, rl = attention_fwd(*sel, causal, window, scale, rows=rows)
+        ref_o.append(ro[0, 0])
+        ref_l.append(rl[0, 0])
+        got_o.append(o[b, h].index_select(0, rows_t).float().cpu().numpy())
+        got_l.append(lse[b, h].index_select(0, rows_t).cpu().numpy())
+    return consistency(np.stack(got_o), np.stack(got_l), np.stack(ref_o), np.stack(ref_l), dtype,
+                       f"{len(rows)} rows (one per block of {rows_block} and the ends) of "
+                       f"(batch, head) {list(picks)}")
+
+
 def time_other_workloads(fa, torch, np, bf, stream, reps: int = 20):
-    """Average kernel time (HIP events) of the other prefill workloads."""
+    """Average kernel time (HIP events) of the other prefill workloads, with
+    the consistency of a sample of each output against the oracle."""
     from io_aware_exact_fa_amd.inputs import prefill_inputs
     res = []
     for name, B, H, Hkv, n, d, causal, window, dt, seed in OTHER_WORKLOADS:
@@ -223,7 +374,13 @@ def time_other_workloads(fa, torch, np, bf, stream, reps: int = 20):
         rec = {"workload": name, "ms": round(ms, 4), "TFLOP/s": round(tf, 2)}
         if dt == "bf16":
             rec["frac_of_bf16_peak"] = round(tf / PEAK_BF16_TFLOPS, 4)
-        log(f"{name}: {ms:.4f} ms  {tf:.1f} TFLOP/s in-band")
+            rec["tiles"] = tile_schedule(n, bool(causal), window, B=B, H=H)
+        rows = np.arange(n) if n <= 256 else stratified_rows(n, 256, seed=seed)
+        rec["consistency"] = dense_consistency(
+            torch, inp, o, lse, bool(causal), window, 1.0 / math.sqrt(d), dt,
+            [(0, 0), (B - 1, H - 1)], rows, 1 if n <= 256 else 256)
+        log(f"{name}: {ms:.4f} ms  {tf:.1f} TFLOP/s in-band  "
+            f"max|dO| {rec['consistency']['max_abs']:.2e} pass={rec['consistency']['pass']}")
         res.append(rec)
         del q, k, v, o, lse
         torch.cuda.empty_cache()
@@ -369,11 +526,34 @@ def time_ragged_workloads(fa, torch, np, bf, stream, reps: int = 20):
         1.0 / math.sqrt(c["d"]), fa.FA_BF16, stream), reps)
     pairs = int((L * (L + 1) // 2).sum()) * c["H"]
     tf = 4 * c["d"] * pairs / (ms * 1e-3) / 1e12
+    # Consistency: the shortest and the longest sequence, two heads, one row
+    # per 256-row block of each (the oracle's per-row definition over that
+    # sequence's keys).
+    from oracle import attention_rows
+    G = c["H"] // c["Hkv"]
+    got_o, got_l, ref_o, ref_l = [], [], [], []
+    for b in (int(np.argmin(L)), int(np.argmax(L))):
+        s0, Lb = int(inp["cu_seqlens"][b]), int(L[b])
+        rows = stratified_rows(Lb, 256, seed=b)
+        for h in (0, c["H"] - 1):
+            g = h // G
+            ro, rl = attention_rows(inp["q"][h, s0 + rows], inp["k"][g, s0:s0 + Lb],
+                                    inp["v"][g, s0:s0 + Lb], rows, True, -1,
+                                    1.0 / math.sqrt(c["d"]))
+            idx = torch.from_numpy(s0 + rows).to(o.device)
+            got_o.append(o[h].index_select(0, idx).float().cpu().numpy())
+            got_l.append(lse[h].index_select(0, idx).cpu().numpy())
+            ref_o.append(ro)
+            ref_l.append(rl)
+    cons = consistency(np.concatenate(got_o), np.concatenate(got_l), np.concatenate(ref_o),
+                       np.concatenate(ref_l), "bf16",
+                       "shortest and longest sequence x heads 0, 31: one row per 256-row block "
+                       "and the ends")
     res.append({"workload": f"ragged causal prefill B{c['B']} H{c['H']}/Hkv{c['Hkv']} d{c['d']} "
                             f"L~U[{c['min_len']},{c['max_len']}] (T={T})",
                 "ms": round(ms, 4), "TFLOP/s": round(tf, 2),
-                "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
-    log(f"{res[-1]['workload']}: {ms:.4f} ms  {tf:.1f} TFLOP/s in-band")
+                "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "consistency": cons})
+    log(f"{res[-1]['workload']}: {ms:.4f} ms  {tf:.1f} TFLOP/s in-band  pass={cons['pass']}")
     del q, k, v, o, lse
 
     c = PAGED
@@ -391,12 +571,41 @@ def time_ragged_workloads(fa, torch, np, bf, stream, reps: int = 20):
         kc.shape[0], 16, pt.shape[1], 1, -1, 1.0 / math.sqrt(c["d"]), fa.FA_BF16, stream), reps)
     pairs = int((C * P + C * (C + 1) // 2).sum()) * c["H"]
     tf = 4 * c["d"] * pairs / (ms * 1e-3) / 1e12
+    # Consistency: the chunks over the shortest and the longest prefix, two
+    # heads, one row per 256 of each chunk; the oracle reads that sequence's
+    # pages (widened from the stored bits) through an identity table.
+    from oracle import gather_paged_kv
+    from io_aware_exact_fa_amd.inputs import bf16_bits_to_f32
+    G = c["H"] // c["Hkv"]
+    Lk = inp["seqlens_k"].astype(np.int64)
+    got_o, got_l, ref_o, ref_l = [], [], [], []
+    for b in (int(np.argmin(P)), int(np.argmax(P))):
+        s0, Cb, Lb = int(inp["cu_seqlens_q"][b]), int(C[b]), int(Lk[b])
+        pb = (Lb + 15) // 16
+        phys = inp["page_table"][b, :pb]
+        kb, vb = gather_paged_kv(bf16_bits_to_f32(inp["kcache_bits"][phys]),
+                                 bf16_bits_to_f32(inp["vcache_bits"][phys]),
+                                 np.arange(pb, dtype=np.int32)[None, :], Lb, 0)
+        rows = stratified_rows(Cb, 256, seed=b)
+        for h in (0, c["H"] - 1):
+            g = h // G
+            ro, rl = attention_rows(inp["q"][h, s0 + rows], kb[g], vb[g], Lb - Cb + rows, True,
+                                    -1, 1.0 / math.sqrt(c["d"]))
+            idx = torch.from_numpy(s0 + rows).to(o.device)
+            got_o.append(o[h].index_select(0, idx).float().cpu().numpy())
+            got_l.append(lse[h].index_select(0, idx).cpu().numpy())
+            ref_o.append(ro)
+            ref_l.append(rl)
+    cons = consistency(np.concatenate(got_o), np.concatenate(got_l), np.concatenate(ref_o),
+                       np.concatenate(ref_l), "bf16",
+                       "chunks over the shortest and longest prefix x heads 0, 31: one row per "
+                       "256 and the ends")
     res.append({"workload": f"chunked causal prefill over 16-token pages B{c['B']} "
                             f"H{c['H']}/Hkv{c['Hkv']} d{c['d']} prefix~U[{c['prefix'][0]},"
                             f"{c['prefix'][1]}] chunk {c['chunk'][0]}",
                 "ms": round(ms, 4), "TFLOP/s": round(tf, 2),
-                "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
-    log(f"{res[-1]['workload']}: {ms:.4f} ms  {tf:.1f} TFLOP/s in-band")
+                "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "consistency": cons})
+    log(f"{res[-1]['workload']}: {ms:.4f} ms  {tf:.1f} TFLOP/s in-band  pass={cons['pass']}")
     del q, kc, vc, o, lse
     torch.cuda.empty_cache()
 
@@ -415,13 +624,29 @@ def time_ragged_workloads(fa, torch, np, bf, stream, reps: int = 20):
     pairs = blocksparse_causal_pairs(lay_np, c["n"], 128, 64)
     tf = 4 * c["d"] * pairs / (ms * 1e-3) / 1e12
     kept = float(lay_np.mean())
+    from oracle import attention_block_sparse
+    rows = stratified_rows(c["n"], 256, seed=c["seed"])
+    idx = torch.from_numpy(rows).to(o.device)
+    got_o, got_l, ref_o, ref_l = [], [], [], []
+    for h in (0, c["H"] - 1):
+        g = h // (c["H"] // c["Hkv"])
+        ro, rl = attention_block_sparse(inp["q"][:, h:h + 1], inp["k"][:, g:g + 1],
+                                        inp["v"][:, g:g + 1], lay_np[h:h + 1], 128, 64, True, -1,
+                                        1.0 / math.sqrt(c["d"]), rows=rows)
+        got_o.append(o[0, h].index_select(0, idx).float().cpu().numpy())
+        got_l.append(lse[0, h].index_select(0, idx).cpu().numpy())
+        ref_o.append(ro[0, 0])
+        ref_l.append(rl[0, 0])
+    cons = consistency(np.stack(got_o), np.stack(got_l), np.stack(ref_o), np.stack(ref_l),
+                       "bf16", f"{rows.size} rows (one per 256-row block and the ends) of heads "
+                               f"0, {c['H'] - 1}")
     res.append({"workload": f"block-sparse causal prefill n{c['n']} H{c['H']}/Hkv{c['Hkv']} "
                             f"d{c['d']}, 128x64 blocks: local +-{c['local']}, first "
                             f"{c['global']} column, {c['density']:.0%} random "
                             f"({kept:.1%} of blocks kept)",
                 "ms": round(ms, 4), "TFLOP/s": round(tf, 2),
-                "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
-    log(f"{res[-1]['workload']}: {ms:.4f} ms  {tf:.1f} TFLOP/s in-band")
+                "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "consistency": cons})
+    log(f"{res[-1]['workload']}: {ms:.4f} ms  {tf:.1f} TFLOP/s in-band  pass={cons['pass']}")
     del q, k, v, o, lse, lay
     torch.cuda.empty_cache()
     return res
@@ -441,7 +666,7 @@ def time_decode_fp8(fa, torch, np, bf, stream, reps: int = 20):
     vs = torch.from_numpy(meta["v_scale"]).to(dev)
     pt = torch.from_numpy(meta["page_table"]).to(dev)
     sl = torch.from_numpy(meta["seqlens"]).to(dev)
-    del meta["kcache8"], meta["vcache8"]
+    k8, v8 = meta.pop("kcache8"), meta.pop("vcache8")
     o = torch.empty_like(q)
     lse = torch.empty((Dc["B"], Dc["H"]), dtype=torch.float32, device=dev)
     ws_bytes = fa.fa_decode_workspace_bytes(Dc["B"], Dc["H"], Dc["max_len"], Dc["d"])
@@ -452,11 +677,24 @@ def time_decode_fp8(fa, torch, np, bf, stream, reps: int = 20):
         stream), reps)
     kv_bytes = int(np.sum(meta["seqlens"].astype(np.int64))) * Dc["Hkv"] * Dc["d"] * 2
     gbs = kv_bytes / (ms * 1e-3) / 1e9
+    from oracle.fp8 import decode_fwd_fp8
+    seqs = decode_sample_seqs(meta["seqlens"])
+    ref_o, ref_l = [], []
+    for b in seqs:
+        pb = (int(meta["seqlens"][b]) + 15) // 16
+        phys = meta["page_table"][b, :pb]
+        ro, rl = decode_fwd_fp8(meta["q"][b:b + 1], k8[phys], v8[phys], meta["k_scale"],
+                                meta["v_scale"], np.arange(pb, dtype=np.int32)[None, :],
+                                meta["seqlens"][b:b + 1], 1.0 / math.sqrt(Dc["d"]))
+        ref_o.append(ro[0])
+        ref_l.append(rl[0])
+    cons = consistency(o.float().cpu().numpy()[seqs], lse.cpu().numpy()[seqs], np.stack(ref_o),
+                       np.stack(ref_l), "bf16", f"sequences {seqs}, every head")
     rec = {"workload": "paged decode B64 H32/Hkv8 d128 L~U[1024,32768] page16, E4M3 K/V "
                        "cache with per-head scales",
            "ms": round(ms, 4), "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-           "kv_bytes": kv_bytes}
-    log(f"{rec['workload']}: {ms:.4f} ms  {gbs:.0f} GB/s of KV")
+           "kv_bytes": kv_bytes, "consistency": cons}
+    log(f"{rec['workload']}: {ms:.4f} ms  {gbs:.0f} GB/s of KV  pass={cons['pass']}")
     del q, kc, vc, o, lse, ws
     torch.cuda.empty_cache()
     return [rec]
@@ -494,9 +732,19 @@ def run_sweep(fa, torch, stream, reps: int = 3):
                        "TFLOP/s": round(tf, 2), "speedup_vs_full": round(full_ms / ms, 2),
                        "pair_ratio_full_over_band": round(inband_pairs(n, False, -1) /
                                                           inband_pairs(n, False, w), 2)}
+                sched = tile_schedule(n, False, w, B=B, H=c["H"])
+                rec["visited_pairs_full_over_band"] = round(
+                    tile_schedule(n, False, -1, B=B, H=c["H"])["visited_pairs"] /
+                    sched["visited_pairs"], 2)
+                rec["inband_over_visited"] = sched["inband_over_visited"]
+                rec["consistency"] = dense_consistency(
+                    torch, {"q": q, "k": k, "v": v}, o, lse, False, w, 1.0 / math.sqrt(c["d"]),
+                    "bf16", [(B - 1, c["H"] - 1)], stratified_rows(n, 512, seed=n + w), 512)
                 res.append(rec)
                 log(f"sweep n={n} w={w} B={B}: {ms:.3f} ms {tf:.1f} TFLOP/s "
-                    f"x{rec['speedup_vs_full']} vs full (pairs x{rec['pair_ratio_full_over_band']})")
+                    f"x{rec['speedup_vs_full']} vs full (pairs x{rec['pair_ratio_full_over_band']}, "
+                    f"visited x{rec['visited_pairs_full_over_band']}) "
+                    f"pass={rec['consistency']['pass']}")
             del q, k, v, o, lse
             torch.cuda.empty_cache()
     return res
@@ -669,6 +917,25 @@ def main():
     import io_aware_exact_fa_amd as fa
     from io_aware_exact_fa_amd.inputs import decode_inputs, prefill_inputs
 
+    P, Dc = PREFILL, DECODE
+    scale = 1.0 / math.sqrt(P["d"])
+    log("generating prefill inputs")
+    pin = prefill_inputs(P["B"], P["H"], P["Hkv"], P["n"], P["d"], seed=P["seed"],
+                         draw_scale=P["draw_scale"])
+    log("generating decode inputs")
+    din = decode_inputs(Dc["B"], Dc["H"], Dc["Hkv"], Dc["d"], Dc["page_size"], Dc["min_len"],
+                        Dc["max_len"], seed=Dc["seed"], with_values=False)
+    # The oracle runs first, before anything touches the GPU: its worker
+    # processes are forked from a process without GPU state (under a profiler
+    # they would otherwise inherit its handlers).  Its outputs are kept for the
+    # consistency check after the timed steps.
+    log("timing the oracle on a bounded sample")
+    cpu_rec, cpu_ref = cpu_baseline(pin, max(1, args.cpu_rows),
+                                    heads=[0, 5, 10, 15, 16, 21, 26, 31])
+    dec_seqs = decode_sample_seqs(din["seqlens"])
+    log(f"decode oracle on sequences {dec_seqs}")
+    dec_ref = decode_oracle_sample(din, dec_seqs, 1.0 / math.sqrt(Dc["d"]))
+
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -678,19 +945,9 @@ def main():
     def i32(x):
         return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(dev)
 
-    P = PREFILL
-    log("generating prefill inputs")
-    pin = prefill_inputs(P["B"], P["H"], P["Hkv"], P["n"], P["d"], seed=P["seed"],
-                         draw_scale=P["draw_scale"])
     q, k, v = bf(pin["q_bits"]), bf(pin["k_bits"]), bf(pin["v_bits"])
     o = torch.empty_like(q)
     lse = torch.empty((P["B"], P["H"], P["n"]), dtype=torch.float32, device=dev)
-    scale = 1.0 / math.sqrt(P["d"])
-
-    Dc = DECODE
-    log("generating decode inputs")
-    din = decode_inputs(Dc["B"], Dc["H"], Dc["Hkv"], Dc["d"], Dc["page_size"], Dc["min_len"],
-                        Dc["max_len"], seed=Dc["seed"], with_values=False)
     dq, dk, dv = bf(din["q_bits"]), bf(din["kcache_bits"]), bf(din["vcache_bits"])
     dpt, dsl = i32(din["page_table"]), i32(din["seqlens"])
     do = torch.empty_like(dq)
@@ -744,6 +1001,41 @@ def main():
     tflops = out["value"]
     log(f"prefill {out['prefill_ms']:.3f} ms  {tflops:.1f} TFLOP/s   decode "
         f"{out['decode_ms']:.3f} ms  {out['decode']['value']:.0f} GB/s")
+
+    # Consistency of the last timed step's outputs with the oracle.
+    rows, heads, o_ref, lse_ref = cpu_ref
+    idx = torch.from_numpy(rows).to(dev)
+    got_o = o[0, heads].index_select(1, idx).float().cpu().numpy()
+    got_l = lse[0, heads].index_select(1, idx).cpu().numpy()
+    out["consistency"] = {
+        "prefill": consistency(got_o, got_l, o_ref[0], lse_ref[0], "bf16",
+                               f"{rows.size} evenly spaced rows x heads {heads} (the cpu "
+                               f"baseline's sample)"),
+        "decode": consistency(do.float().cpu().numpy()[dec_seqs], dlse.cpu().numpy()[dec_seqs],
+                              dec_ref[0], dec_ref[1], "bf16",
+                              f"sequences {dec_seqs}, every head"),
+    }
+    log(f"consistency: prefill {out['consistency']['prefill']}  decode "
+        f"{out['consistency']['decode']}")
+
+    # The block skip observed on the device: one counting launch (not timed)
+    # against the host replica of the schedule.
+    cnt = torch.zeros(2, dtype=torch.int64, device=dev)
+    o2 = torch.empty_like(o)
+    lse2 = torch.empty_like(lse)
+    fa.fa_fwd_tile_count(q, k, v, o2, lse2, P["B"], P["H"], P["Hkv"], P["n"], P["d"],
+                         P["causal"], P["window"], scale, cnt, stream)
+    torch.cuda.synchronize()
+    sched = tile_schedule(P["n"], bool(P["causal"]), P["window"], B=P["B"], H=P["H"])
+    got = cnt.cpu().tolist()
+    sched["device_visited_wave_tiles"] = int(got[0])
+    sched["device_staged_tiles"] = int(got[1])
+    sched["device_matches_schedule"] = (got[0] == sched["visited_wave_tiles"] and
+                                        got[1] == sched["staged_tiles"])
+    sched["outputs_equal_fa_fwd"] = bool(torch.equal(o, o2) and torch.equal(lse, lse2))
+    out["tiles"] = sched
+    log(f"tiles: {sched}")
+    del o2, lse2
     if args.clock_seconds > 0:
         log(f"sampling the GFX clock over {args.clock_seconds:g} s of prefill launches")
         clk = sustained_clock(torch, prefill, args.clock_seconds)
@@ -766,9 +1058,7 @@ def main():
                                   time_decode_fp8(fa, torch, np, bf, stream))
     if args.sweep:
         out["sweep"] = run_sweep(fa, torch, stream)
-    log("timing the oracle on a bounded sample")
-    out["cpu_baseline"] = cpu_baseline(pin, max(1, args.cpu_rows),
-                                       heads=[0, 5, 10, 15, 16, 21, 26, 31])
+    out["cpu_baseline"] = cpu_rec
     print(json.dumps(out), flush=True)
 
 

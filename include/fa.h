@@ -18,6 +18,8 @@
  *   fa_fwd_blocksparse  fa_fwd restricted to the kept blocks of a layout.
  *   fa_decode_fp8  fa_decode over an FP8 (E4M3) key/value cache.
  *   fa_fwd_strided fa_fwd over caller-strided tensors (e.g. BSHD).
+ *   fa_fwd_tile_count  fa_fwd (bf16) that also counts the key tiles it
+ *              visits and stages (the skip, observed on the device).
  *
  * Sources (web pages on IO-aware exact attention):
  *   - charles2530 blog "算子与编译器：FlashAttention 与长上下文": §1 (the
@@ -99,6 +101,30 @@ typedef enum {
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int Hkv, int n, int d, int causal, int window,
            float scale, int dtype, void* stream);
+
+/*
+ * fa_fwd_tile_count -- fa_fwd with dtype FA_BF16 that also counts, on the
+ * device, what the block skip leaves to do.  The pages' sliding-window
+ * prefill article (xxqk.cn, §9.1 and §9.3) asks to check which key/value
+ * blocks the kernel really computes and reads; this entry point reports
+ * both.  The outputs o and lse are bit for bit those of fa_fwd.
+ *
+ *   counters  DEVICE, two uint64 values, ADDED to (the caller zeroes them):
+ *             counters[0] += number of (wave, key tile) pairs whose products
+ *                            are computed; a wave owns 32 query rows and a
+ *                            key tile is 64 keys, so 2048 (query, key) pairs
+ *                            each;
+ *             counters[1] += number of 64-key K/V tiles staged into on-chip
+ *                            memory (one per workgroup and tile visited).
+ *
+ * The counting adds one atomic per wave and tile: a diagnostic launch, not
+ * for timing.  Limits and errors as fa_fwd with dtype FA_BF16, plus
+ * FA_ERR_NULL when counters is NULL.
+ */
+int fa_fwd_tile_count(const void* q, const void* k, const void* v, void* o,
+                      float* lse, int B, int H, int Hkv, int n, int d,
+                      int causal, int window, float scale,
+                      unsigned long long* counters, void* stream);
 
 /*
  * fa_fwd_varlen -- attention forward over a ragged batch (sequences of
@@ -248,10 +274,11 @@ size_t fa_decode_workspace_bytes(int B, int H, int max_seqlen, int d);
  * tokens are left out).  Both only keep memory accesses in bounds: the
  * result for such input is not attention over the intended cache.
  *
- * Limits: B, H, Hkv >= 1; H % Hkv == 0; H / Hkv <= 16; d == 128;
- * page_size == 16; num_pages >= 1; max_pages >= 1; max_seqlen >= 1.
- * Errors: FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE,
- * FA_ERR_LAUNCH.
+ * Limits: B, H, Hkv >= 1; H % Hkv == 0; H / Hkv <= 16; d == 64 or 128;
+ * page_size == 16; num_pages >= 1; max_pages >= 1; max_seqlen >= 1;
+ * B * H, B * max_pages and max_pages * 16 below 2^31.
+ * Errors: FA_ERR_NULL, FA_ERR_SHAPE (sizes), FA_ERR_UNSUPPORTED (d,
+ * page_size or H / Hkv), FA_ERR_WORKSPACE, FA_ERR_LAUNCH.
  */
 int fa_decode(const void* q, const void* kcache, const void* vcache,
               const int32_t* page_table, const int32_t* seqlens, void* o,
@@ -306,7 +333,10 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
  *                   infinities; S.1111.111 is NaN)
  *   k_scale, v_scale [Hkv] float32, DEVICE: per key/value head
  *                   dequantisation scales, k = byte * k_scale[g],
- *                   v = byte * v_scale[g]
+ *                   v = byte * v_scale[g]; any finite value, zero included
+ *                   (a head quantised from an all-zero cache: its scores are
+ *                   all 0 and its softmax uniform) and negative values; a
+ *                   non-finite scale gives a non-finite result for its head
  *   everything else as fa_decode (q bf16, page_table, seqlens, o bf16, lse,
  *   workspace of fa_decode_workspace_bytes(B, H, max_seqlen, d) bytes).
  *

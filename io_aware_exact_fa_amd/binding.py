@@ -71,6 +71,9 @@ def lib() -> ctypes.CDLL:
     L.fa_fwd_strided.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                  f32, i32, vp]
     L.fa_fwd_strided.restype = i32
+    L.fa_fwd_tile_count.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                    f32, vp, vp]
+    L.fa_fwd_tile_count.restype = i32
     L.fa_strerror.argtypes = [i32]
     L.fa_strerror.restype = ctypes.c_char_p
     L.fa_version.argtypes = []
@@ -112,6 +115,17 @@ def fa_fwd(q, k, v, o, lse, B, H, Hkv, n, d, causal, window, scale, dtype,
                       float(scale), int(dtype), _stream(stream))
     if st != 0:
         raise FaError(st, "fa_fwd")
+
+
+def fa_fwd_tile_count(q, k, v, o, lse, B, H, Hkv, n, d, causal, window, scale, counters,
+                      stream=None) -> None:
+    """Raw C-ABI call (bf16 forward that adds its visited / staged key-tile
+    counts to the two uint64 ``counters``); tensors or device addresses."""
+    st = lib().fa_fwd_tile_count(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
+                                 int(Hkv), int(n), int(d), int(causal), int(window),
+                                 float(scale), _ptr(counters), _stream(stream))
+    if st != 0:
+        raise FaError(st, "fa_fwd_tile_count")
 
 
 def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, H, Hkv, total, max_seqlen, d, causal,

@@ -84,10 +84,15 @@ __device__ __forceinline__ int decode_len(const DecodeArgs& a, int b) {
 // the prefill kernel: the result is unchanged, most pages skip the rescale.
 constexpr float kDecodeRescaleThreshold = 8.0f;
 
-// Swizzle of the 16-byte chunks of a V page row in LDS (16 rows x 256 B):
-// chunk c of row r sits at c ^ vswz(r), so the transposed reads of one
-// instruction (16 rows x 32 B) spread over all banks in two passes.
-__device__ __forceinline__ int vswz(int r) { return 2 * (r & 7); }
+// Swizzle of the 16-byte chunks of a V page row in LDS (16 rows x 2*D bytes):
+// chunk c of row r sits at c ^ vswz<D>(r), so the transposed reads of one
+// instruction (16 rows x 32 B) spread over the banks.  The XOR value is even,
+// so chunks 2k and 2k+1 stay side by side (the FP8 path writes them as one
+// widened 16-byte piece).
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+  return D == 128 ? 2 * (r & 7) : 2 * (r & 3);
+}
 
 // Range-checked view of one (page, KV head) slab: loads at offsets past
 // nbytes return zeros without touching memory, so a prefetch past the last
@@ -125,10 +130,12 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(u32x2 w) {
 
 template <int D, int GP, bool FP8>
 __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeArgs a) {
-  static_assert(D == 128, "decode kernel is written for head dim 128");
+  static_assert(D == 128 || D == 64, "head dim 64 or 128");
   constexpr int NC = D / 32;   // 32-dim chunks of the QK contraction
   constexpr int NDB = D / 16;  // 16-dim blocks of the PV output
   constexpr int PAGE_BYTES = kPage * D * 2;
+  constexpr int CPR = D / 8;   // 16-byte bf16 chunks per page row
+  constexpr int NVJ = PAGE_BYTES / 1024;  // 1 KB V DMA instructions per page
   // Per wave: two V page buffers (double-buffered), filled by LDS DMA.
   __shared__ __attribute__((aligned(1024))) char sV0[kDecodeWaves][PAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char sV1[kDecodeWaves][PAGE_BYTES];
@@ -187,26 +194,26 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
   }
 
   // V DMA: lane i of instruction j writes LDS slot 64*j + i (16 B), which holds
-  // physical chunk slot%16 of page row slot/16.
-  unsigned v_off[4];
+  // physical chunk slot%CPR of page row slot/CPR.
+  unsigned v_off[NVJ];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < NVJ; ++j) {
     const int slot = 64 * j + lane;
-    const int r = slot >> 4;
-    const int c = (slot & 15) ^ vswz(r);
+    const int r = slot / CPR;
+    const int c = (slot % CPR) ^ vswz<D>(r);
     v_off[j] = (unsigned)(r * D * 2 + c * 16);
   }
   // Transposed V read (block db): lane supplies row 4*grp + (lane%16)/4,
   // dims 16*db + 4*(lane%4) .. +4 (8 bytes).
   const int vr_row = 4 * grp + ((lane & 15) >> 2);
-  const int vr_sw = vswz(vr_row);
+  const int vr_sw = vswz<D>(vr_row);
 
   struct PageK {
     bf16x8 k[NC];
   };
   struct PageK8 {  // FP8: the page's key and value bytes held by this lane
-    u32x4 k[NC / 2];  // token col, dims 64m + 16*grp .. +15
-    u32x4 v[2];       // 16-byte piece 64j + lane of the page (row-major)
+    u32x4 k[NC / 2];   // token col, dims 64m + 16*grp .. +15
+    u32x4 v[D / 64];   // 16-byte piece 64j + lane of the page (row-major)
   };
   using PageRegs = typename std::conditional<FP8, PageK8, PageK>::type;
   auto phys_of = [&](int i) {
@@ -231,7 +238,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
         r.k[m] = __builtin_bit_cast(
             u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, col * D + 64 * m + 16 * grp, 0, 0));
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < D / 64; ++j)
         r.v[j] = __builtin_bit_cast(
             u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, 1024 * j + 16 * lane, 0, 0));
     } else {
@@ -244,7 +251,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
         r.k[j] = __builtin_bit_cast(
             bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, 1024 * j + 16 * lane, 0, 0));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dma16(rv, v_off[j], vdst + 1024 * j);
+      for (int j = 0; j < NVJ; ++j) dma16(rv, v_off[j], vdst + 1024 * j);
     }
   };
 
@@ -262,9 +269,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
       // bf16 chunks 2k and 2k+1, which the swizzle (an XOR with an even
       // value) keeps side by side.
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int piece = 64 * j + lane, r8 = piece >> 3, k8 = piece & 7;
-        char* dst = const_cast<char*>(vsrc) + r8 * D * 2 + 16 * ((2 * k8) ^ vswz(r8));
+      for (int j = 0; j < D / 64; ++j) {
+        const int piece = 64 * j + lane, r8 = piece / (D / 16), k8 = piece % (D / 16);
+        char* dst = const_cast<char*>(vsrc) + r8 * D * 2 + 16 * ((2 * k8) ^ vswz<D>(r8));
         *reinterpret_cast<bf16x8*>(dst) = e4m3x8_to_bf16(u32x2{r.v[j][0], r.v[j][1]});
         *reinterpret_cast<bf16x8*>(dst + 16) = e4m3x8_to_bf16(u32x2{r.v[j][2], r.v[j][3]});
       }
@@ -274,33 +281,39 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
         kf[2 * m + 1] = e4m3x8_to_bf16(u32x2{r.k[m][2], r.k[m][3]});
       }
     } else {
-      // Piece j of lane l is row 4j + l/16, 16-byte chunk l%16; it is stored
-      // at chunk (l%16) ^ (row%16) of its row, so that the fragment reads
-      // (16 rows, one chunk each) fall on distinct banks.
+      // Piece j of lane l is row (64j + l)/CPR, 16-byte chunk l%CPR; it is
+      // stored at chunk (l%CPR) ^ (row%CPR) of its row, so that the fragment
+      // reads (16 rows, one chunk each) spread over the banks.
       char* ks = sK[FP8 ? 0 : wave];
 #pragma unroll
       for (int j = 0; j < NC; ++j) {
-        const int kr = 4 * j + (lane >> 4);
-        *reinterpret_cast<bf16x8*>(ks + kr * D * 2 + 16 * ((lane & 15) ^ (kr & 15))) = r.k[j];
+        const int kr = (64 * j + lane) / CPR;
+        *reinterpret_cast<bf16x8*>(ks + kr * D * 2 + 16 * ((lane % CPR) ^ (kr % CPR))) = r.k[j];
       }
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        kf[c] = *reinterpret_cast<const bf16x8*>(ks + col * D * 2 + 16 * ((4 * c + grp) ^ (col & 15)));
+        kf[c] = *reinterpret_cast<const bf16x8*>(ks + col * D * 2 +
+                                                 16 * ((4 * c + grp) ^ (col % CPR)));
     }
 
     // S^T = K Q^T: lane (col q, grp) holds tokens 4*grp + rr of query q.
     f32x4 sc = f32x4{};
 #pragma unroll
     for (int c = 0; c < NC; ++c) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[c], qf[c], sc, 0, 0, 0);
+    // Scores in base-2 units, scaled before the mask: the FP8 key scale may
+    // be zero (a head quantised from zeros) or negative, and -inf * 0 or a
+    // max taken before a negative scale would be wrong.
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) sc[rr] *= c2;
     if (tail) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr)
         if (tok0 + 4 * grp + rr >= lim) sc[rr] = kNegInf;
     }
     float mx = __builtin_fmaxf(__builtin_fmaxf(sc[0], sc[1]), __builtin_fmaxf(sc[2], sc[3]));
-    mx = max_xor32(max_xor16(mx)) * c2;
+    mx = max_xor32(max_xor16(mx));
     const bool need = mx > m_ref + kDecodeRescaleThreshold;
     if (__builtin_amdgcn_ballot_w64(need)) {
       const float alpha = need ? exp2_fast(m_ref - mx) : 1.f;
@@ -313,7 +326,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
     bf16x4 pb;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      const float pv = exp2_fast(__builtin_fmaf(sc[rr], c2, -m_use));
+      const float pv = exp2_fast(sc[rr] - m_use);
       l_part += pv;
       pb[rr] = (__bf16)pv;
     }
@@ -400,11 +413,13 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
 
 // Merge of the split partials of one (b, h): 4 waves.  The workgroup first
 // finds the largest partial lse; wave w then sums splits w, w+4, ... with weights
-// exp2(lse_e - max), each lane owning two head dims; the waves' sums are
+// exp2(lse_e - max), each lane owning D/64 head dims; the waves' sums are
 // added through LDS.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
-  static_assert(D == 128, "two head dims per lane");
+  static_assert(D == 128 || D == 64, "one or two head dims per lane");
+  constexpr int DPL = D / 64;
+  typedef float fdpl __attribute__((ext_vector_type(DPL)));
   __shared__ float red[4];
   __shared__ float part_o[4][D];
   __shared__ float part_w[4];
@@ -424,44 +439,53 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   __syncthreads();
   M = fmax2(fmax2(red[0], red[1]), fmax2(red[2], red[3]));
   const float Mu = (M == kNegInf) ? 0.f : M;
-  float W = 0.f, o0 = 0.f, o1 = 0.f;
+  float W = 0.f;
+  float ov_acc[DPL];
+#pragma unroll
+  for (int u = 0; u < DPL; ++u) ov_acc[u] = 0.f;
+  auto part = [&](int e) {
+    return *reinterpret_cast<const fdpl*>(o_e + (size_t)e * D + DPL * lane);
+  };
   int e = wave;
   for (; e + 12 < ne; e += 16) {
     float w[4];
-    f32x2 x[4];
+    fdpl x[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       w[u] = exp2_fast(lse_e[e + 4 * u] - Mu);
-      x[u] = *reinterpret_cast<const f32x2*>(o_e + (size_t)(e + 4 * u) * D + 2 * lane);
+      x[u] = part(e + 4 * u);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       W += w[u];
-      o0 = __builtin_fmaf(w[u], x[u][0], o0);
-      o1 = __builtin_fmaf(w[u], x[u][1], o1);
+#pragma unroll
+      for (int c = 0; c < DPL; ++c) ov_acc[c] = __builtin_fmaf(w[u], x[u][c], ov_acc[c]);
     }
   }
   for (; e < ne; e += 4) {
     const float w = exp2_fast(lse_e[e] - Mu);
-    const f32x2 x = *reinterpret_cast<const f32x2*>(o_e + (size_t)e * D + 2 * lane);
+    const fdpl x = part(e);
     W += w;
-    o0 = __builtin_fmaf(w, x[0], o0);
-    o1 = __builtin_fmaf(w, x[1], o1);
+#pragma unroll
+    for (int c = 0; c < DPL; ++c) ov_acc[c] = __builtin_fmaf(w, x[c], ov_acc[c]);
   }
-  part_o[wave][2 * lane] = o0;
-  part_o[wave][2 * lane + 1] = o1;
+#pragma unroll
+  for (int c = 0; c < DPL; ++c) part_o[wave][DPL * lane + c] = ov_acc[c];
   if (lane == 0) part_w[wave] = W;
   __syncthreads();
   if (wave != 0) return;
   const float Wt = part_w[0] + part_w[1] + part_w[2] + part_w[3];
   const float inv = Wt > 0.f ? 1.f / Wt : 0.f;
-  bf16x2 ov;
+  __bf16 ov[DPL];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int d = 2 * lane + u;
+  for (int u = 0; u < DPL; ++u) {
+    const int d = DPL * lane + u;
     ov[u] = (__bf16)((part_o[0][d] + part_o[1][d] + part_o[2][d] + part_o[3][d]) * inv);
   }
-  *reinterpret_cast<bf16x2*>(a.o + (size_t)bh * D + 2 * lane) = ov;
+  if constexpr (DPL == 2)
+    *reinterpret_cast<bf16x2*>(a.o + (size_t)bh * D + 2 * lane) = bf16x2{ov[0], ov[1]};
+  else
+    a.o[(size_t)bh * D + lane] = ov[0];
   if (lane == 0) a.lse[bh] = Wt > 0.f ? (Mu + log2_fast(Wt)) * kLn2 : kNegInf;
 }
 
@@ -499,30 +523,38 @@ size_t decode_workspace_bytes(int B, int H, int max_seqlen, int d) {
   return align_up(rows * d * sizeof(float), 256) + align_up(rows * sizeof(float), 256);
 }
 
-template <int GP, bool FP8>
+template <int D, int GP, bool FP8>
 static void launch_split(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<128, GP, FP8>), dim3(a.max_splits, a.Hkv, a.B),
+  hipLaunchKernelGGL((decode_split_kernel<D, GP, FP8>), dim3(a.max_splits, a.Hkv, a.B),
                      dim3(kDecodeWaves * 64), 0, stream, a);
+}
+
+template <int D, bool FP8>
+static hipError_t launch_decode_d(DecodeArgs& a, int B, int H, void* workspace,
+                                  hipStream_t stream) {
+  const size_t rows = (size_t)B * H * a.max_splits;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                      align_up(rows * D * sizeof(float), 256));
+  const int G = a.G;
+  if (G <= 1) launch_split<D, 1, FP8>(a, stream);
+  else if (G <= 2) launch_split<D, 2, FP8>(a, stream);
+  else if (G <= 4) launch_split<D, 4, FP8>(a, stream);
+  else if (G <= 8) launch_split<D, 8, FP8>(a, stream);
+  else if (G <= 16) launch_split<D, 16, FP8>(a, stream);
+  else return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(B * H), dim3(256), 0, stream, a);
+  return hipGetLastError();
 }
 
 template <bool FP8>
 static hipError_t launch_decode_t(DecodeArgs& a, int B, int H, int d, void* workspace,
                                   hipStream_t stream) {
-  const size_t rows = (size_t)B * H * a.max_splits;
-  a.ws_o = static_cast<float*>(workspace);
-  a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                      align_up(rows * d * sizeof(float), 256));
-  const int G = a.G;
-  if (G <= 1) launch_split<1, FP8>(a, stream);
-  else if (G <= 2) launch_split<2, FP8>(a, stream);
-  else if (G <= 4) launch_split<4, FP8>(a, stream);
-  else if (G <= 8) launch_split<8, FP8>(a, stream);
-  else if (G <= 16) launch_split<16, FP8>(a, stream);
-  else return hipErrorInvalidValue;
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(B * H), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  if (d == 128) return launch_decode_d<128, FP8>(a, B, H, workspace, stream);
+  if (d == 64) return launch_decode_d<64, FP8>(a, B, H, workspace, stream);
+  return hipErrorInvalidValue;
 }
 
 static DecodeArgs decode_args(const void* q, const int32_t* page_table, const int32_t* seqlens,
@@ -548,7 +580,6 @@ hipError_t launch_decode_fp8(const void* q, const void* kcache, const void* vcac
                              float* lse, int B, int H, int Hkv, int d, int num_pages,
                              int max_pages, int max_seqlen, float scale, void* workspace,
                              hipStream_t stream) {
-  if (d != 128) return hipErrorInvalidValue;
   DecodeArgs a = decode_args(q, page_table, seqlens, o, lse, B, H, Hkv, num_pages, max_pages,
                              max_seqlen, scale);
   a.kc8 = static_cast<const unsigned char*>(kcache);
@@ -562,7 +593,6 @@ hipError_t launch_decode(const void* q, const void* kcache, const void* vcache,
                          const int32_t* page_table, const int32_t* seqlens, void* o, float* lse,
                          int B, int H, int Hkv, int d, int num_pages, int max_pages,
                          int max_seqlen, float scale, void* workspace, hipStream_t stream) {
-  if (d != 128) return hipErrorInvalidValue;
   DecodeArgs a = decode_args(q, page_table, seqlens, o, lse, B, H, Hkv, num_pages, max_pages,
                              max_seqlen, scale);
   a.kc = static_cast<const __bf16*>(kcache);

@@ -66,6 +66,26 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+int fa_fwd_tile_count(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                      int H, int Hkv, int n, int d, int causal, int window, float scale,
+                      unsigned long long* counters, void* stream) {
+  if (!counters) return FA_ERR_NULL;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || Hkv < 1 || n < 1 || d < 1) return FA_ERR_SHAPE;
+  if (H % Hkv != 0) return FA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
+  if (!scale_ok(scale)) return FA_ERR_SHAPE;
+  if (!fits_i32((long long)n * d)) return FA_ERR_SHAPE;
+  if (!fits_i32((long long)B * H) || !grid_ok(n, B, H)) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (window < 0) window = -1;
+  if (window > n) window = n;
+  hipError_t e = fa::launch_prefill_bf16_counted(q, k, v, o, lse, B, H, Hkv, n, d, causal, window,
+                                                 scale, counters,
+                                                 static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                   const int32_t* cu_seqlens, int B, int H, int Hkv, int total, int max_seqlen,
                   int d, int causal, int window, float scale, int dtype, void* stream) {
@@ -183,8 +203,10 @@ int fa_decode(const void* q, const void* kcache, const void* vcache, const int32
     return FA_ERR_SHAPE;
   if (H % Hkv != 0) return FA_ERR_SHAPE;
   if (!scale_ok(scale)) return FA_ERR_SHAPE;
-  if (!fits_i32((long long)B * H) || !fits_i32((long long)B * max_pages)) return FA_ERR_SHAPE;
-  if (d != 128 || page_size != 16 || H / Hkv > 16) return FA_ERR_UNSUPPORTED;
+  if (!fits_i32((long long)B * H) || !fits_i32((long long)B * max_pages) ||
+      !fits_i32((long long)max_pages * 16))
+    return FA_ERR_SHAPE;
+  if ((d != 64 && d != 128) || page_size != 16 || H / Hkv > 16) return FA_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < fa::decode_workspace_bytes(B, H, max_seqlen, d))
     return FA_ERR_WORKSPACE;
   hipError_t e = fa::launch_decode(q, kcache, vcache, page_table, seqlens, o, lse, B, H, Hkv, d,
@@ -205,8 +227,10 @@ int fa_decode_fp8(const void* q, const void* kcache, const void* vcache, const f
     return FA_ERR_SHAPE;
   if (H % Hkv != 0) return FA_ERR_SHAPE;
   if (!scale_ok(scale)) return FA_ERR_SHAPE;
-  if (!fits_i32((long long)B * H) || !fits_i32((long long)B * max_pages)) return FA_ERR_SHAPE;
-  if (d != 128 || page_size != 16 || H / Hkv > 16) return FA_ERR_UNSUPPORTED;
+  if (!fits_i32((long long)B * H) || !fits_i32((long long)B * max_pages) ||
+      !fits_i32((long long)max_pages * 16))
+    return FA_ERR_SHAPE;
+  if ((d != 64 && d != 128) || page_size != 16 || H / Hkv > 16) return FA_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < fa::decode_workspace_bytes(B, H, max_seqlen, d))
     return FA_ERR_WORKSPACE;
   hipError_t e = fa::launch_decode_fp8(q, kcache, vcache, k_scale, v_scale, page_table, seqlens,

@@ -14,6 +14,12 @@ namespace fa {
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* o,
                                float* lse, int B, int H, int Hkv, int n, int d,
                                int causal, int window, float scale, hipStream_t stream);
+// As launch_prefill_bf16, and counters[0] += (wave, key tile) pairs whose
+// products are computed, counters[1] += key/value tiles staged (device).
+hipError_t launch_prefill_bf16_counted(const void* q, const void* k, const void* v, void* o,
+                                       float* lse, int B, int H, int Hkv, int n, int d,
+                                       int causal, int window, float scale,
+                                       unsigned long long* counters, hipStream_t stream);
 // Ragged batch: q, o [H, total, d]; k, v [Hkv, total, d]; lse [H, total];
 // cu_seqlens [B+1] device offsets.
 hipError_t launch_prefill_bf16_varlen(const void* q, const void* k, const void* v, void* o,

@@ -104,6 +104,9 @@ struct PrefillArgs {
   int q_ss, kv_ss, o_ss;
   // 1: each workgroup runs query blocks NQ-1-t and t (causal load balance)
   int pair;
+  // Counting launches only: [0] += (wave, key tile) pairs whose products are
+  // computed, [1] += key/value tiles staged into LDS.
+  unsigned long long* counters;
 };
 
 // LDS tiles are dense (no padding): row r of a tile holds D bf16 values as
@@ -135,7 +138,7 @@ __device__ __forceinline__ void buffer_load_lds16(const void* base, int nbytes, 
 // probabilities stay <= 2^8 and most tiles skip the accumulator rescale.
 constexpr float kRescaleThreshold = 8.0f;
 
-template <int D, int NW, int BC, int MODE>
+template <int D, int NW, int BC, int MODE, bool COUNT = false>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int BR = NW * 32;         // query rows per workgroup (32 per wave)
   constexpr int RB = D * 2;           // bytes per tile row
@@ -330,6 +333,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillAr
     auto page_id = [&](int kt) { return pt[min(kt * 4 + wave_u / WPP, last_page)]; };
     auto stage = [&](int kt, char* tk, char* tv, int pid) {
       const int k0 = kt * BC;
+      if constexpr (COUNT) {
+        if (tid == 0) atomicAdd(&a.counters[1], 1ull);
+      }
       if constexpr (MODE != kPaged) {
         (void)pid;
         // the descriptor ends after the tile's last row inside the sequence:
@@ -383,6 +389,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillAr
       const bool active = wave_rows && !(k1 < wlo0 || k0 > whi1);
       const bool full = (k0 >= wlo1) && (k1 <= whi0);
       if (!active) return;
+      if constexpr (COUNT) {
+        if (lane == 0) atomicAdd(&a.counters[0], 1ull);
+      }
       // S^T = K Q^T; the K fragments of the next head-dim chunk are read while
       // the current chunk's MFMAs run.
       auto kfrag = [&](int dc, int kb) {
@@ -486,6 +495,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillAr
       const int lh = a.layout_heads == 1 ? 0 : h;
       const unsigned char* lay =
           a.layout + ((size_t)lh * a.nqb + qb) * (size_t)a.layout_cols;
+      // A paired workgroup builds a second list here: every wave must have
+      // read the first block's count before wave 0 overwrites it (a block
+      // with no kept tile runs no barrier in its loop).
+      if (a.pair) __syncthreads();
       if (wave_u == 0) {
         int cnt = 0;
         for (int c0 = kt_lo; c0 <= kt_hi; c0 += 64) {
@@ -564,7 +577,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillAr
   if (qb_second >= 0) query_block(qb_second);
 }
 
-template <int D, int MODE, int NW>
+template <int D, int MODE, int NW, bool COUNT = false>
 static hipError_t launch_nw(const PrefillArgs& a0, int rows, hipStream_t stream) {
   constexpr int BC = 64;
   constexpr int BR = NW * 32;
@@ -578,8 +591,8 @@ static hipError_t launch_nw(const PrefillArgs& a0, int rows, hipStream_t stream)
   a.pair = a.causal && (MODE == kDense || MODE == kStrided || MODE == kBlockSparse) &&
            (long long)a.nqb * a.B * a.H < 16 * kResident;
   const long long grid = (long long)(a.pair ? (a.nqb + 1) / 2 : a.nqb) * a.B * a.H;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, BC, MODE>), dim3((unsigned)grid), dim3(NW * 64),
-                     0, stream, a);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, BC, MODE, COUNT>), dim3((unsigned)grid),
+                     dim3(NW * 64), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -594,14 +607,14 @@ static hipError_t launch_nw(const PrefillArgs& a0, int rows, hipStream_t stream)
 // faster).  Ragged batches measured the same either way (each sequence's
 // partly filled last block offsets the gain) and block-sparse layouts are
 // defined over 128-row blocks: four waves for both.
-template <int D, int MODE>
+template <int D, int MODE, bool COUNT = false>
 static hipError_t launch_d(const PrefillArgs& a, int rows, hipStream_t stream) {
   if constexpr (MODE == kDense || MODE == kStrided || MODE == kPaged) {
     const long long keys_per_row =
         a.window < 0 ? (1LL << 62) : (a.causal ? a.window + 1LL : 2LL * a.window + 1);
-    if (keys_per_row >= 16384) return launch_nw<D, MODE, 8>(a, rows, stream);
+    if (keys_per_row >= 16384) return launch_nw<D, MODE, 8, COUNT>(a, rows, stream);
   }
-  return launch_nw<D, MODE, 4>(a, rows, stream);
+  return launch_nw<D, MODE, 4, COUNT>(a, rows, stream);
 }
 
 static PrefillArgs base_args(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -628,6 +641,18 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void
   a.n = n;
   if (d == 128) return launch_d<128, kDense>(a, n, stream);
   if (d == 64) return launch_d<64, kDense>(a, n, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_bf16_counted(const void* q, const void* k, const void* v, void* o,
+                                       float* lse, int B, int H, int Hkv, int n, int d,
+                                       int causal, int window, float scale,
+                                       unsigned long long* counters, hipStream_t stream) {
+  PrefillArgs a = base_args(q, k, v, o, lse, B, H, Hkv, causal, window, scale);
+  a.n = n;
+  a.counters = counters;
+  if (d == 128) return launch_d<128, kDense, true>(a, n, stream);
+  if (d == 64) return launch_d<64, kDense, true>(a, n, stream);
   return hipErrorInvalidValue;
 }
 

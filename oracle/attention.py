@@ -165,13 +165,21 @@ def attention_fwd(q, k, v, causal: bool = False, window: int = -1,
                 o[tb, th, off:off + len(rc)] = ob
                 lse[tb, th, off:off + len(rc)] = lb
         else:
+            # Workers are forked (they inherit the inputs without copying) and
+            # end by returning from their task loop once the pool is closed;
+            # they are never sent a signal (a profiler's handlers, inherited
+            # through fork, must not run in them).
             ctx = _mp.get_context("fork")
-            with ctx.Pool(workers, initializer=_worker_init) as pool:
+            pool = ctx.Pool(workers, initializer=_worker_init)
+            try:
                 for (tb, th, _), off, res in zip(
                         tasks, offsets, pool.imap(_task, tasks, chunksize=1)):
                     _, _, rc, ob, lb = res
                     o[tb, th, off:off + len(rc)] = ob
                     lse[tb, th, off:off + len(rc)] = lb
+            finally:
+                pool.close()
+                pool.join()
     finally:
         _SHARED.clear()
     return o, lse

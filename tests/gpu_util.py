@@ -113,3 +113,79 @@ def compare_grad(got, ref, bound, label, tol=TOL_BWD, fro=True):
     if fro and got.size // got.shape[-1] >= 256:
         assert rel_fro <= tol["rel_fro"], f"{label}: relative Frobenius error {rel_fro}"
 
+
+
+def decode_oracle_all(meta, scale, fp8: bool = False, batches=None):
+    """The decode oracle over every sequence (or ``batches``), one sequence at
+    a time: each call gets that sequence's own pages (converted from the
+    stored bf16 bits or E4M3 bytes) and an identity table over them, so the
+    whole cache is never widened to float at once."""
+    from oracle import decode_fwd
+    from oracle.fp8 import decode_fwd_fp8
+    from io_aware_exact_fa_amd.inputs import bf16_bits_to_f32
+    sl = np.asarray(meta["seqlens"])
+    B, H, d = meta["q"].shape
+    o = np.zeros((B, H, d))
+    lse = np.zeros((B, H))
+    ps = meta["page_size"]
+    for b in (range(B) if batches is None else batches):
+        L = int(sl[b])
+        pb = (L + ps - 1) // ps
+        phys = meta["page_table"][b, :pb]
+        table = np.arange(pb, dtype=np.int32)[None, :]
+        if fp8:
+            ob, lb = decode_fwd_fp8(meta["q"][b:b + 1], meta["kcache8"][phys],
+                                    meta["vcache8"][phys], meta["k_scale"], meta["v_scale"],
+                                    table, sl[b:b + 1], scale)
+        else:
+            ob, lb = decode_fwd(meta["q"][b:b + 1], bf16_bits_to_f32(meta["kcache_bits"][phys]),
+                                bf16_bits_to_f32(meta["vcache_bits"][phys]), table,
+                                sl[b:b + 1], scale)
+        o[b], lse[b] = ob[0], lb[0]
+    return o, lse
+
+
+def oracle_workers() -> int:
+    """Host processes for the oracle in the GPU tests: the cores this process
+    may use, at most 16."""
+    from oracle.attention import default_workers
+    return max(1, min(16, default_workers()))
+
+
+_ROWS_FN = None
+
+
+def _rows_task(chunk):
+    return _ROWS_FN(chunk)
+
+
+def oracle_rows_parallel(fn, rows, chunk: int = 256):
+    """fn(rows_subset) -> (o [..., R, d], lse [..., R]) evaluated over ``rows``
+    in chunks on forked worker processes (the oracle's own arithmetic, only
+    spread over cores); results concatenated along the row axis."""
+    import multiprocessing as mp
+    global _ROWS_FN
+    rows = np.asarray(rows)
+    chunks = [rows[i:i + chunk] for i in range(0, rows.size, chunk)]
+    _ROWS_FN = fn
+    try:
+        pool = mp.get_context("fork").Pool(min(oracle_workers(), len(chunks)))
+        try:
+            res = pool.map(_rows_task, chunks, chunksize=1)
+        finally:
+            pool.close()
+            pool.join()
+    finally:
+        _ROWS_FN = None
+    return (np.concatenate([r[0] for r in res], axis=-2),
+            np.concatenate([r[1] for r in res], axis=-1))
+
+
+def stratified_rows(n: int, block: int, seed: int, extra=()):
+    """One seeded row from every ``block``-row block of [0, n), plus ``extra``."""
+    rng = np.random.default_rng(seed)
+    starts = np.arange(0, n, block)
+    picks = starts + rng.integers(0, block, size=starts.size)
+    rows = set(int(r) for r in picks if r < n)
+    rows.update(int(r) for r in extra if 0 <= r < n)
+    return np.array(sorted(rows))

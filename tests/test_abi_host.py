@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"fa_fwd", "fa_decode", "fa_decode_workspace_bytes",
                           "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_varlen", "fa_fwd_paged",
                           "fa_fwd_blocksparse", "fa_decode_fp8", "fa_fwd_strided",
-                          "fa_strerror", "fa_version"}
+                          "fa_fwd_tile_count", "fa_strerror", "fa_version"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -69,6 +69,26 @@ def test_fwd_rejects(lib, kw, status):
     assert _fwd(**kw) == status
 
 
+def _count(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=2, H=8, Hkv=2, n=1000, d=128,
+                causal=1, window=-1, scale=0.1, counters=FAKE)
+    args.update(kw)
+    return fa.lib().fa_fwd_tile_count(args["q"], args["k"], args["v"], args["o"], args["lse"],
+                                      args["B"], args["H"], args["Hkv"], args["n"], args["d"],
+                                      args["causal"], args["window"],
+                                      ctypes.c_float(args["scale"]), args["counters"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(counters=None), -1), (dict(q=None), -1), (dict(lse=None), -1),
+    (dict(B=0), -2), (dict(n=0), -2), (dict(H=3, Hkv=2), -2), (dict(causal=2), -2),
+    (dict(scale=0.0), -2), (dict(n=1 << 25, d=128), -2),
+    (dict(d=96), -3),
+])
+def test_tile_count_rejects(lib, kw, status):
+    assert _count(**kw) == status
+
+
 def _dec(**kw):
     args = dict(q=FAKE, kc=FAKE, vc=FAKE, pt=FAKE, sl=FAKE, o=FAKE, lse=FAKE, B=2, H=8,
                 Hkv=2, d=128, P=10, ps=16, maxp=4, maxs=64, scale=0.1, ws=FAKE,
@@ -85,7 +105,8 @@ def _dec(**kw):
     (dict(sl=None), -1), (dict(o=None), -1), (dict(lse=None), -1),
     (dict(B=0), -2), (dict(H=0), -2), (dict(Hkv=0), -2), (dict(P=0), -2), (dict(ps=0), -2),
     (dict(maxp=0), -2), (dict(maxs=0), -2), (dict(H=6, Hkv=4), -2), (dict(scale=0.0), -2),
-    (dict(d=64), -3), (dict(ps=32), -3), (dict(H=34, Hkv=2), -3),
+    (dict(maxp=1 << 28), -2),  # max_pages * 16 overflows 32 bits
+    (dict(d=96), -3), (dict(d=256), -3), (dict(ps=32), -3), (dict(H=34, Hkv=2), -3),
     (dict(ws=None), -4), (dict(wsb=16), -4),
 ])
 def test_decode_rejects(lib, kw, status):
@@ -226,7 +247,8 @@ def _dec8(**kw):
     (dict(lse=None), -1),
     (dict(B=0), -2), (dict(H=0), -2), (dict(Hkv=0), -2), (dict(P=0), -2), (dict(maxs=0), -2),
     (dict(H=6, Hkv=4), -2), (dict(scale=-1.0), -2),
-    (dict(d=64), -3), (dict(ps=8), -3), (dict(H=34, Hkv=2), -3),
+    (dict(maxp=1 << 28), -2),  # max_pages * 16 overflows 32 bits
+    (dict(d=96), -3), (dict(ps=8), -3), (dict(H=34, Hkv=2), -3),
     (dict(ws=None), -4), (dict(wsb=16), -4),
 ])
 def test_decode_fp8_rejects(lib, kw, status):

@@ -164,3 +164,54 @@ def test_sustained_clock_uses_the_mean_over_xcds(monkeypatch):
 def test_host_cpu_model_is_a_string():
     m = bench.host_cpu_model()
     assert isinstance(m, str) and m
+
+
+def brute_tiles(n, causal, window, nw):
+    """(visited (wave, tile) pairs, staged (workgroup, tile) pairs) by explicit
+    enumeration: a wave visits a 64-key tile when one of its 32 rows sees a
+    key in it; a workgroup of nw waves stages the tiles any of its rows sees."""
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    vis = np.ones((n, n), dtype=bool)
+    if causal:
+        vis &= j <= i
+    if window >= 0:
+        vis &= (j >= i - window) if causal else (np.abs(i - j) <= window)
+    nt = -(-n // 64)
+    tile_hit = np.zeros((n, nt), dtype=bool)
+    for t in range(nt):
+        tile_hit[:, t] = vis[:, t * 64:(t + 1) * 64].any(axis=1)
+    visited = sum(int(tile_hit[r:r + 32].any(axis=0).sum()) for r in range(0, n, 32))
+    staged = sum(int(tile_hit[r:r + 32 * nw].any(axis=0).sum()) for r in range(0, n, 32 * nw))
+    return visited, staged
+
+
+@pytest.mark.parametrize("n", [1, 63, 64, 65, 300, 700])
+@pytest.mark.parametrize("causal", [False, True])
+def test_tile_schedule_matches_enumeration(n, causal):
+    for w in sorted({-1, 0, 1, 37, 64, 100, n - 1, n}):
+        if w < -1:
+            continue
+        s = bench.tile_schedule(n, causal, w, B=2, H=3)
+        v, st = brute_tiles(n, causal, w, s["waves_per_workgroup"])
+        assert s["visited_wave_tiles"] == 6 * v, (n, causal, w)
+        assert s["staged_tiles"] == 6 * st, (n, causal, w)
+        assert s["inband_pairs"] == 6 * brute_pairs(n, causal, w)
+        assert s["visited_pairs"] >= s["inband_pairs"]
+
+
+def test_tile_schedule_workloads():
+    # Long causal: 8-wave workgroups; each wave's last tile straddles the
+    # diagonal, so the matrix cores evaluate a little more than n(n+1)/2.
+    s = bench.tile_schedule(65536, True, -1, H=32)
+    assert s["waves_per_workgroup"] == 8
+    assert s["inband_pairs"] == 32 * 65536 * 65537 // 2
+    assert 0.998 < s["inband_over_visited"] < 1.0
+    # Band w = 2048: 4-wave workgroups; an interior wave's 32 rows see a
+    # 4128-key union, 65 tiles of 64 keys, for 4097 visible keys per row.
+    s = bench.tile_schedule(32768, False, 2048, H=32)
+    assert s["waves_per_workgroup"] == 4
+    assert 0.98 < s["inband_over_visited"] < 0.99
+    # A large window on the 8-wave rule's edge.
+    assert bench.tile_schedule(40000, True, 16383)["waves_per_workgroup"] == 8
+    assert bench.tile_schedule(40000, True, 16382)["waves_per_workgroup"] == 4

@@ -3,8 +3,8 @@
 Small shapes over every output (rows whose kept blocks hold no visible key
 must come back as o = 0, lse = -inf exactly); the band layout with the window
 must reproduce fa_fwd with that window bit for bit (same tiles, same
-arithmetic); a 32768-token layout with local, global and random blocks on
-sampled rows.
+arithmetic); a 32768-token layout with local, global and random blocks over
+two whole heads and one row of every block of every head.
 """
 
 import math
@@ -14,7 +14,8 @@ import pytest
 
 from io_aware_exact_fa_amd.inputs import block_layout, prefill_inputs
 from oracle.blocksparse import attention_block_sparse
-from tests.gpu_util import TOL_BF16, compare, dev_bf16, prefill_device, say
+from tests.gpu_util import (TOL_BF16, compare, dev_bf16, oracle_rows_parallel,
+                             prefill_device, say, stratified_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -88,9 +89,26 @@ def test_band_layout_equals_windowed_forward_bitwise(causal, window):
     assert np.array_equal(lse, l2.cpu().numpy())
 
 
-def test_blocksparse_full_size_sampled():
+def test_blocksparse_paired_grid_empty_first_block():
+    """Short causal grids pair query blocks (a workgroup runs block NQ-1-t,
+    then t).  With the first block of every pair empty (no kept tile, so no
+    barrier in its tile loop), the workgroup's second block list must still
+    be built only after every wave has read the first block's count."""
+    B, H, Hkv, n, d = 2, 4, 2, 1024, 128
+    inp = prefill_inputs(B, H, Hkv, n, d, seed=5200)
+    lay = block_layout(H, n, 128, 64, seed=5201, density=0.5)
+    lay[:, 4:, :] = 0  # blocks 4..7, the first of each pair (7-t, t), keep nothing
+    scale = 1.0 / math.sqrt(d)
+    o, lse = run_bs(inp, lay, 64, 1, -1, scale)
+    o_ref, lse_ref = attention_block_sparse(inp["q"], inp["k"], inp["v"], lay, 128, 64, True, -1,
+                                            scale)
+    check(o, lse, o_ref, lse_ref, "bs paired, first blocks empty")
+
+
+def test_blocksparse_full_size():
     """n = 32768, 32 heads sharing 8 KV heads: one local block either side of the
-    diagonal, the first key block column, 10 % random blocks, causal."""
+    diagonal, the first key block column, 10 % random blocks, causal.  Two
+    whole heads, and in every head one row of every 128-row block plus edges."""
     B, H, Hkv, n, d = 1, 32, 8, 32768, 128
     say("blocksparse full n=32768")
     inp = prefill_inputs(B, H, Hkv, n, d, seed=13)
@@ -98,10 +116,18 @@ def test_blocksparse_full_size_sampled():
     scale = 1.0 / math.sqrt(d)
     o, lse = run_bs(inp, lay, 64, 1, -1, scale)
     assert np.isfinite(o).all() and np.isfinite(lse).all()
-    rng = np.random.default_rng(7)
-    rows = np.unique(np.concatenate([[0, 1, 127, 128, 16383, n - 1], rng.integers(0, n, 10)]))
-    for h in (0, 13, H - 1):
-        o_ref, l_ref = attention_block_sparse(inp["q"][:, h:h + 1], inp["k"][:, h // 4:h // 4 + 1],
-                                              inp["v"][:, h // 4:h // 4 + 1], lay[h:h + 1], 128,
-                                              64, True, -1, scale, rows=rows)
-        check(o[:, h:h + 1, rows], lse[:, h:h + 1, rows], o_ref, l_ref, f"bs full h{h}")
+    for h in (0, H - 1):
+        g = h // (H // Hkv)
+
+        def head_rows(rows, h=h, g=g):
+            return attention_block_sparse(inp["q"][:, h:h + 1], inp["k"][:, g:g + 1],
+                                          inp["v"][:, g:g + 1], lay[h:h + 1], 128, 64, True, -1,
+                                          scale, rows=rows)
+
+        o_ref, l_ref = oracle_rows_parallel(head_rows, np.arange(n), chunk=512)
+        check(o[:, h:h + 1], lse[:, h:h + 1], o_ref, l_ref, f"bs full h{h} (every row)")
+    rows = stratified_rows(n, 128, seed=7, extra=[0, 1, 127, 128, 16383, n - 1])
+    o_ref, l_ref = oracle_rows_parallel(
+        lambda r: attention_block_sparse(inp["q"], inp["k"], inp["v"], lay, 128, 64, True, -1,
+                                         scale, rows=r), rows, chunk=16)
+    check(o[:, :, rows], lse[:, :, rows], o_ref, l_ref, f"bs full all heads, {rows.size} rows")
