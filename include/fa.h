@@ -287,6 +287,34 @@ int fa_decode(const void* q, const void* kcache, const void* vcache,
               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fa_decode_noalloc -- fa_decode for callers that cannot allocate device
+ * memory (code under stream capture, tight serving loops, harnesses that
+ * forbid allocation): no workspace argument.  The split partials live in a
+ * fixed array inside the library, 32 MiB (FA_DECODE_NOALLOC_MAX_BYTES) on
+ * each GPU the library runs on, held until the process ends.  The call makes
+ * no allocation of any kind.
+ *
+ *   Arguments, results and limits as fa_decode, without workspace and
+ *   workspace_bytes.  The partials must fit:
+ *   fa_decode_workspace_bytes(B, H, max_seqlen, d) <= FA_DECODE_NOALLOC_MAX_BYTES
+ *   (for instance B = 64, H = 32, max_seqlen = 32768, d = 128 needs 23 MB);
+ *   otherwise FA_ERR_WORKSPACE and nothing is enqueued.
+ *
+ * Every call on one GPU uses that GPU's one array: calls that overlap on the
+ * same GPU (several streams, or several host threads, before the earlier
+ * call's kernels have finished) race and give wrong results.  Calls in order
+ * on one stream are safe; each call overwrites what the previous one left.
+ * Errors: as fa_decode; FA_ERR_LAUNCH also when the array's device address
+ * cannot be obtained.
+ */
+#define FA_DECODE_NOALLOC_MAX_BYTES ((size_t)32 << 20)
+int fa_decode_noalloc(const void* q, const void* kcache, const void* vcache,
+                      const int32_t* page_table, const int32_t* seqlens, void* o,
+                      float* lse, int B, int H, int Hkv, int d, int num_pages,
+                      int page_size, int max_pages, int max_seqlen, float scale,
+                      void* stream);
+
+/*
  * fa_bwd_workspace_bytes -- device workspace fa_bwd needs for these sizes
  * (one float per query row: D_i = <dO_i, O_i>).  0 if out of range.
  */

@@ -13,5 +13,5 @@ from .binding import (  # noqa: F401
     fa_fwd_varlen, fa_fwd_paged, fa_strerror, fa_version, flash_attn_fwd, flash_decode,
     flash_attn_bwd, flash_attn_varlen, flash_attn_paged, fa_fwd_blocksparse,
     flash_attn_blocksparse, fa_decode_fp8, flash_decode_fp8, fa_fwd_strided,
-    flash_attn_strided, fa_fwd_tile_count,
+    flash_attn_strided, fa_fwd_tile_count, fa_decode_noalloc,
 )

@@ -74,6 +74,9 @@ def lib() -> ctypes.CDLL:
     L.fa_fwd_tile_count.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                     f32, vp, vp]
     L.fa_fwd_tile_count.restype = i32
+    L.fa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                    i32, i32, i32, f32, vp]
+    L.fa_decode_noalloc.restype = i32
     L.fa_strerror.argtypes = [i32]
     L.fa_strerror.restype = ctypes.c_char_p
     L.fa_version.argtypes = []
@@ -115,6 +118,18 @@ def fa_fwd(q, k, v, o, lse, B, H, Hkv, n, d, causal, window, scale, dtype,
                       float(scale), int(dtype), _stream(stream))
     if st != 0:
         raise FaError(st, "fa_fwd")
+
+
+def fa_decode_noalloc(q, kcache, vcache, page_table, seqlens, o, lse, B, H, Hkv, d, num_pages,
+                      page_size, max_pages, max_seqlen, scale, stream=None) -> None:
+    """Raw C-ABI call: fa_decode with the split partials in the library's own
+    static device array (no workspace, no allocation)."""
+    st = lib().fa_decode_noalloc(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(page_table),
+                                 _ptr(seqlens), _ptr(o), _ptr(lse), int(B), int(H), int(Hkv),
+                                 int(d), int(num_pages), int(page_size), int(max_pages),
+                                 int(max_seqlen), float(scale), _stream(stream))
+    if st != 0:
+        raise FaError(st, "fa_decode_noalloc")
 
 
 def fa_fwd_tile_count(q, k, v, o, lse, B, H, Hkv, n, d, causal, window, scale, counters,

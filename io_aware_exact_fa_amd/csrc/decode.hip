@@ -45,6 +45,7 @@
 //     registers); the key scale joins the score scale and the value scale
 //     multiplies the split's output.  Half the bytes of the bf16 cache move.
 
+#include <mutex>
 #include <type_traits>
 
 #include "common.hpp"
@@ -587,6 +588,51 @@ hipError_t launch_decode_fp8(const void* q, const void* kcache, const void* vcac
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   return launch_decode_t<true>(a, B, H, d, workspace, stream);
+}
+
+// ---- allocation-free decode: split partials in a static device array ----
+//
+// For callers that cannot allocate device memory.  Each GPU the library runs
+// on holds one copy of this array until the process ends; the kernels get it
+// as their workspace pointer like any caller-owned buffer.  Every call on a
+// device shares that device's copy, so calls that overlap on one GPU race.
+// Every partial the merge reads is written by the split kernel of the same
+// call, so nothing needs clearing between calls.
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+// The array's device address on the current device, looked up once per
+// device (the host-side name is only a stand-in for the symbol).
+static hipError_t scratch_address(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_decode_static(const void* q, const void* kcache, const void* vcache,
+                                const int32_t* page_table, const int32_t* seqlens, void* o,
+                                float* lse, int B, int H, int Hkv, int d, int num_pages,
+                                int max_pages, int max_seqlen, float scale,
+                                hipStream_t stream) {
+  if (decode_workspace_bytes(B, H, max_seqlen, d) > kDecodeScratchBytes)
+    return hipErrorInvalidValue;
+  void* ws = nullptr;
+  hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return e;
+  return launch_decode(q, kcache, vcache, page_table, seqlens, o, lse, B, H, Hkv, d, num_pages,
+                       max_pages, max_seqlen, scale, ws, stream);
 }
 
 hipError_t launch_decode(const void* q, const void* kcache, const void* vcache,

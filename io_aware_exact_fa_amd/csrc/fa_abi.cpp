@@ -12,6 +12,9 @@
 
 #include "launch.hpp"
 
+static_assert(FA_DECODE_NOALLOC_MAX_BYTES == fa::kDecodeScratchBytes,
+              "the header states the library's static decode array size");
+
 namespace {
 
 bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
@@ -212,6 +215,28 @@ int fa_decode(const void* q, const void* kcache, const void* vcache, const int32
   hipError_t e = fa::launch_decode(q, kcache, vcache, page_table, seqlens, o, lse, B, H, Hkv, d,
                                    num_pages, max_pages, max_seqlen, scale, workspace,
                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_decode_noalloc(const void* q, const void* kcache, const void* vcache,
+                      const int32_t* page_table, const int32_t* seqlens, void* o, float* lse,
+                      int B, int H, int Hkv, int d, int num_pages, int page_size, int max_pages,
+                      int max_seqlen, float scale, void* stream) {
+  if (!q || !kcache || !vcache || !page_table || !seqlens || !o || !lse) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || Hkv < 1 || d < 1 || num_pages < 1 || page_size < 1 || max_pages < 1 ||
+      max_seqlen < 1)
+    return FA_ERR_SHAPE;
+  if (H % Hkv != 0) return FA_ERR_SHAPE;
+  if (!scale_ok(scale)) return FA_ERR_SHAPE;
+  if (!fits_i32((long long)B * H) || !fits_i32((long long)B * max_pages) ||
+      !fits_i32((long long)max_pages * 16))
+    return FA_ERR_SHAPE;
+  if ((d != 64 && d != 128) || page_size != 16 || H / Hkv > 16) return FA_ERR_UNSUPPORTED;
+  if (fa::decode_workspace_bytes(B, H, max_seqlen, d) > fa::kDecodeScratchBytes)
+    return FA_ERR_WORKSPACE;
+  hipError_t e = fa::launch_decode_static(q, kcache, vcache, page_table, seqlens, o, lse, B, H,
+                                          Hkv, d, num_pages, max_pages, max_seqlen, scale,
+                                          static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -66,6 +66,15 @@ hipError_t launch_decode(const void* q, const void* kcache, const void* vcache,
                          float* lse, int B, int H, int Hkv, int d, int num_pages,
                          int max_pages, int max_seqlen, float scale, void* workspace,
                          hipStream_t stream);
+// Decode with the split partials in the library's static device array
+// (kDecodeScratchBytes per device) instead of a caller workspace; fails with
+// hipErrorInvalidValue when the partials would not fit.
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+hipError_t launch_decode_static(const void* q, const void* kcache, const void* vcache,
+                                const int32_t* page_table, const int32_t* seqlens, void* o,
+                                float* lse, int B, int H, int Hkv, int d, int num_pages,
+                                int max_pages, int max_seqlen, float scale,
+                                hipStream_t stream);
 
 // Backward: delta workspace [B,H,n] floats; window clamped as for prefill.
 size_t bwd_workspace_bytes(int B, int H, int n);

@@ -33,7 +33,8 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"fa_fwd", "fa_decode", "fa_decode_workspace_bytes",
                           "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_varlen", "fa_fwd_paged",
                           "fa_fwd_blocksparse", "fa_decode_fp8", "fa_fwd_strided",
-                          "fa_fwd_tile_count", "fa_strerror", "fa_version"}
+                          "fa_fwd_tile_count", "fa_decode_noalloc", "fa_strerror",
+                          "fa_version"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -67,6 +68,34 @@ def _fwd(**kw):
 ])
 def test_fwd_rejects(lib, kw, status):
     assert _fwd(**kw) == status
+
+
+def _dec_na(**kw):
+    args = dict(q=FAKE, kc=FAKE, vc=FAKE, pt=FAKE, sl=FAKE, o=FAKE, lse=FAKE, B=2, H=8,
+                Hkv=2, d=128, P=10, ps=16, maxp=4, maxs=64, scale=0.1)
+    args.update(kw)
+    return fa.lib().fa_decode_noalloc(args["q"], args["kc"], args["vc"], args["pt"], args["sl"],
+                                      args["o"], args["lse"], args["B"], args["H"], args["Hkv"],
+                                      args["d"], args["P"], args["ps"], args["maxp"],
+                                      args["maxs"], ctypes.c_float(args["scale"]), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(pt=None), -1), (dict(lse=None), -1),
+    (dict(B=0), -2), (dict(maxs=0), -2), (dict(H=6, Hkv=4), -2), (dict(scale=0.0), -2),
+    (dict(maxp=1 << 28), -2),
+    (dict(d=96), -3), (dict(ps=32), -3), (dict(H=34, Hkv=2), -3),
+    # partials beyond the 32 MiB array: 128 sequences x 32 heads at 32K tokens
+    (dict(B=128, H=32, Hkv=8, maxp=2048, maxs=32768), -4),
+])
+def test_decode_noalloc_rejects(lib, kw, status):
+    assert _dec_na(**kw) == status
+
+
+def test_decode_noalloc_limit_matches_workspace_size(lib):
+    limit = 32 << 20
+    assert fa.fa_decode_workspace_bytes(64, 32, 32768, 128) <= limit   # the decode workload
+    assert fa.fa_decode_workspace_bytes(128, 32, 32768, 128) > limit
 
 
 def _count(**kw):
