@@ -169,7 +169,9 @@ def oracle_rows_parallel(fn, rows, chunk: int = 256):
     chunks = [rows[i:i + chunk] for i in range(0, rows.size, chunk)]
     _ROWS_FN = fn
     try:
-        pool = mp.get_context("fork").Pool(min(oracle_workers(), len(chunks)))
+        from oracle.attention import _worker_init  # one BLAS thread per worker process
+        pool = mp.get_context("fork").Pool(min(oracle_workers(), len(chunks)),
+                                           initializer=_worker_init)
         try:
             res = pool.map(_rows_task, chunks, chunksize=1)
         finally:
