@@ -706,7 +706,7 @@ SWEEP = dict(n=(4096, 8192, 16384, 32768), window=(512, 1024, 2048, -1), batch=(
              H=32, Hkv=32, d=128, seed=14)
 
 
-def run_sweep(fa, torch, stream, reps: int = 3):
+def run_sweep(fa, torch, stream, reps: int = 5):
     """Time fa_fwd over the sweep; returns one record per (n, window, batch)."""
     c = SWEEP
     res = []
@@ -723,7 +723,7 @@ def run_sweep(fa, torch, stream, reps: int = 3):
             for w in sorted(c["window"], key=lambda x: x < 0, reverse=True):  # full first
                 ms = _time(torch, stream, lambda: fa.fa_fwd(
                     q, k, v, o, lse, B, c["H"], c["Hkv"], n, c["d"], 0, w,
-                    1.0 / math.sqrt(c["d"]), fa.FA_BF16, stream), reps, warm_seconds=0.0)
+                    1.0 / math.sqrt(c["d"]), fa.FA_BF16, stream), reps, warm_seconds=0.25)
                 pairs = inband_pairs(n, False, w) * B * c["H"]
                 tf = 4 * c["d"] * pairs / (ms * 1e-3) / 1e12
                 if w < 0:
