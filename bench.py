@@ -145,7 +145,9 @@ def measured_traffic(kernel_key: str, src_hash: str):
 
 KERNEL_KEYS = {  # traffic.json key -> (kernel-name patterns, sources)
     # The dense prefill and the dQ kernel are instantiated per wave count.
-    "prefill_bf16": ((r"prefill_bf16_kernel<128, \d+, 64, 0>",), ("prefill_bf16.hip", "common.hpp")),
+    # The dense prefill kernel without its counting variant (template flag false).
+    "prefill_bf16": ((r"prefill_bf16_kernel<128, \d+, 64, 0, false>",),
+                     ("prefill_bf16.hip", "common.hpp")),
     "decode": ((r"decode_split_kernel<128, 4, false>", r"decode_combine_kernel"),
                ("decode.hip", "common.hpp")),
     "backward": ((r"bwd_delta_kernel<128>", r"bwd_dkdv_kernel<128>", r"bwd_dq_kernel<128(, \d+)?>"),
@@ -164,14 +166,18 @@ def traffic_from_counters(fetch_csv: str, write_csv: str) -> dict:
 
     def per_kernel(path, counter):
         vals = defaultdict(list)
-        calib = []
+        copies = []
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] != counter:
                 continue
             name, v = r["Kernel_Name"], float(r["Counter_Value"])
-            if "copyBuffer" in name and int(r["Grid_Size"]) >= 65536:
-                calib.append(v)
+            if "copyBuffer" in name:
+                copies.append((int(r["Grid_Size"]), v))
             vals[name].append(v)
+        # The calibration copy is the largest device copy of the run (the other
+        # copies move a few KiB to a few MiB of results and counters).
+        top = max((g for g, _ in copies), default=None)
+        calib = [v for g, v in copies if g == top]
         return vals, calib
 
     out = {"_about": "HBM traffic per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE "

@@ -287,6 +287,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillAr
     for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
     float m_ref = kNegInf;  // reference max (base-2 scaled units) of this lane's row
     float l_run = 0.f;      // this lane's share of the row sum (pair with lane ^ 32)
+    // Counting launches: this wave's visited tiles and (wave 0) staged tiles,
+    // added to the device counters once per query block.
+    unsigned visited = 0, staged = 0;
 
     // ---- direct HBM -> LDS staging of one K/V tile ----
     // Wave instruction j writes 64 consecutive 16-byte slots; slot s holds
@@ -333,9 +336,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillAr
     auto page_id = [&](int kt) { return pt[min(kt * 4 + wave_u / WPP, last_page)]; };
     auto stage = [&](int kt, char* tk, char* tv, int pid) {
       const int k0 = kt * BC;
-      if constexpr (COUNT) {
-        if (tid == 0) atomicAdd(&a.counters[1], 1ull);
-      }
+      if constexpr (COUNT) staged += 1;
       if constexpr (MODE != kPaged) {
         (void)pid;
         // the descriptor ends after the tile's last row inside the sequence:
@@ -389,9 +390,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillAr
       const bool active = wave_rows && !(k1 < wlo0 || k0 > whi1);
       const bool full = (k0 >= wlo1) && (k1 <= whi0);
       if (!active) return;
-      if constexpr (COUNT) {
-        if (lane == 0) atomicAdd(&a.counters[0], 1ull);
-      }
+      if constexpr (COUNT) visited += 1;
       // S^T = K Q^T; the K fragments of the next head-dim chunk are read while
       // the current chunk's MFMAs run.
       auto kfrag = [&](int dc, int kb) {
@@ -551,6 +550,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillAr
       __syncthreads();
     }
 
+    if constexpr (COUNT) {
+      if (lane == 0) {
+        if (visited) atomicAdd(&a.counters[0], (unsigned long long)visited);
+        if (wave_u == 0 && staged) atomicAdd(&a.counters[1], (unsigned long long)staged);
+      }
+    }
     // ---- epilogue: O = acc / l, lse = ln(2) * (m + log2 l) ----
     if (!wave_rows) return;
     const float lt = sum_xor32(l_run);

@@ -215,3 +215,42 @@ def test_tile_schedule_workloads():
     # A large window on the 8-wave rule's edge.
     assert bench.tile_schedule(40000, True, 16383)["waves_per_workgroup"] == 8
     assert bench.tile_schedule(40000, True, 16382)["waves_per_workgroup"] == 4
+
+
+def _counter_csv(path, counter, rows):
+    import csv
+    cols = ["Correlation_Id", "Dispatch_Id", "Grid_Size", "Kernel_Name", "Counter_Name",
+            "Counter_Value"]
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(cols)
+        for i, (grid, name, value) in enumerate(rows):
+            w.writerow([i, i, grid, name, counter, value])
+
+
+def test_traffic_from_counters_calibrates_on_the_largest_copy(tmp_path):
+    """The counters are scaled by the bench's 256 MiB copy (the largest copy
+    of the run), whatever other small copies the run made."""
+    pre = "void fa::prefill_bf16_kernel<128, 8, 64, 0, false>(fa::PrefillArgs)"
+    cnt = "void fa::prefill_bf16_kernel<128, 8, 64, 0, true>(fa::PrefillArgs)"
+    dec = ["void fa::decode_split_kernel<128, 4, false>(fa::DecodeArgs)",
+           "void fa::decode_combine_kernel<128>(fa::DecodeArgs)"]
+    bwd = ["void fa::bwd_delta_kernel<128>(fa::BwdArgs)", "void fa::bwd_dkdv_kernel<128>(fa::BwdArgs)",
+           "void fa::bwd_dq_kernel<128, 8>(fa::BwdArgs)"]
+    copy = "__amd_rocclr_copyBuffer"
+    fetch = [(512, copy, 2.6), (131072, copy, 131072.0), (65536, copy, 523.5), (4096, copy, 44.5),
+             (8192, pre, 1000.0), (8192, pre, 1002.0), (8192, cnt, 5000.0),
+             (512, dec[0], 10.0), (64, dec[1], 1.0)] + [(8, b, 7.0) for b in bwd]
+    write = [(131072, copy, 262144.0), (65536, copy, 1000.0), (8192, pre, 100.0), (8192, cnt, 900.0),
+             (512, dec[0], 2.0), (64, dec[1], 3.0)] + [(8, b, 5.0) for b in bwd]
+    fp, wp = tmp_path / "f.csv", tmp_path / "w.csv"
+    _counter_csv(fp, "FETCH_SIZE", fetch)
+    _counter_csv(wp, "WRITE_SIZE", write)
+    rec = bench.traffic_from_counters(str(fp), str(wp))
+    assert rec["scale"] == {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
+    # prefill: mean of its two (uncounted) dispatches, scaled
+    assert rec["prefill_bf16"]["fetch_size_bytes"] == int(1001.0 * 1024 * 2.0)
+    assert rec["prefill_bf16"]["write_size_bytes"] == int(100.0 * 1024)
+    # decode: split + merge per launch
+    assert rec["decode"]["bytes_per_launch"] == int(11.0 * 1024 * 2.0 + 5.0 * 1024)
+    assert rec["backward"]["bytes_per_launch"] == int(21.0 * 1024 * 2.0 + 15.0 * 1024)
