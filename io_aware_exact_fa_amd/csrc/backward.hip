@@ -141,15 +141,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int IPW = BQ * CPR / (64 * NW);
   constexpr int NDC = D / 16, NDB = D / 32;
   static_assert(BQ * CPR % (64 * NW) == 0, "tile must split evenly over waves");
-  __shared__ __attribute__((aligned(1024))) char sQ0[TILE];
-  __shared__ __attribute__((aligned(1024))) char sO0[TILE];
-  __shared__ __attribute__((aligned(1024))) char sQ1[TILE];
-  __shared__ __attribute__((aligned(1024))) char sO1[TILE];
-  // lse and D of the staged query rows (64 slots, the first BQ used).
-  __shared__ __attribute__((aligned(256))) float sL0[64];
-  __shared__ __attribute__((aligned(256))) float sD0[64];
-  __shared__ __attribute__((aligned(256))) float sL1[64];
-  __shared__ __attribute__((aligned(256))) float sD1[64];
+  // Three stage buffers, each one LDS object holding a Q tile, a dO tile,
+  // then lse and D of the staged query rows (64 slots each, the first BQ
+  // used).  One object per stage lets the compiler tell the buffer being read
+  // from those that in-flight loads fill.
+  constexpr int STAGE = 2 * TILE + 2 * 64 * 4;
+  __shared__ __attribute__((aligned(1024))) char sB0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char sB1[STAGE];
+  __shared__ __attribute__((aligned(1024))) char sB2[STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -214,32 +213,47 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // innermost: the workgroups of one (b, g) that an XCD runs together start
   // on the same tiles, and a replacement workgroup starts where the others
   // started shortly before, so Q and dO tiles are mostly read from L2 (a key
-  // block further down simply stops earlier).
-  auto head_of = [&](int t) { return g * G + t % G; };
-  auto qtile_of = [&](int t) { return qt_hi - t / G; };
-  auto stage = [&](int t, char* tq, char* to, float* tl, float* td) {
-    const int h = head_of(t), q0 = qtile_of(t) * BQ;
+  // block further down simply stops earlier).  Step t is (query head
+  // g*G + t%G, query tile qt_hi - t/G); a cursor holds both and moves one step.
+  struct Cursor {
+    int hq, qt;
+  };
+  auto advance = [&](Cursor& c) __attribute__((always_inline)) {
+    if (++c.hq == G) {
+      c.hq = 0;
+      --c.qt;
+    }
+  };
+  // Every step stages one (Q, dO, lse, D) tile; a step past the last one
+  // issues the same loads with an empty descriptor (no memory access), so
+  // that each wave has the same number of loads in flight on every path.
+  // Even waves load lse, odd waves D (waves 2 and 3 repeat the values 0 and 1
+  // write).  Rows past n read as zero.
+  auto stage = [&](int t, const Cursor& c, char* buf) __attribute__((always_inline)) {
+    const bool live = t < T;
+    const int h = g * G + c.hq, q0 = max(c.qt, 0) * BQ;
     const size_t row0 = (size_t)(b * a.H + h) * n + q0;
-    const int bytes = (n - q0) * RB;
+    const int bytes = live ? (n - q0) * RB : 0;
 #pragma unroll
     for (int j = 0; j < IPW; ++j) {
-      bwd_load_lds16(a.q + row0 * D, bytes, st_off[j], tq + (wave * IPW + j) * 1024);
-      bwd_load_lds16(a.dout + row0 * D, bytes, st_off[j], to + (wave * IPW + j) * 1024);
+      bwd_load_lds16(a.q + row0 * D, bytes, st_off[j], buf + (wave * IPW + j) * 1024);
+      bwd_load_lds16(a.dout + row0 * D, bytes, st_off[j], buf + TILE + (wave * IPW + j) * 1024);
     }
-    // 4 bytes per lane: lane i's float lands at tl[i] / td[i]; rows past n read 0.
-    if (wave == 0)
-      bwd_load_lds4(a.lse + row0, (n - q0) * 4, 4u * lane, tl);
-    else if (wave == 1)
-      bwd_load_lds4(a.delta + row0, (n - q0) * 4, 4u * lane, td);
+    const float* src = (wave & 1) ? a.delta : a.lse;
+    bwd_load_lds4(src + row0, live ? (n - q0) * 4 : 0, 4u * lane,
+                  buf + 2 * TILE + 256 * (wave & 1));
   };
 
   const float c2 = a.scale_log2;
   const float log2e = kLog2e;
 
-  auto tile = [&](int t, const char* Qs, const char* Os, const float* Ls, const float* Ds)
-                  __attribute__((always_inline)) {
+  auto tile = [&](int qt, const char* buf) __attribute__((always_inline)) {
     if (!wave_keys) return;
-    const int q0 = qtile_of(t) * BQ;
+    const char* Qs = buf;
+    const char* Os = buf + TILE;
+    const float* Ls = reinterpret_cast<const float*>(buf + 2 * TILE);
+    const float* Ds = Ls + 64;
+    const int q0 = qt * BQ;
     const int q1 = min(q0 + BQ, n) - 1;
     // band test over this wave's keys [kw0, kw1] and the tile's queries [q0, q1]
     if (hi_of(q1) < kw0 || lo_of(q0) > kw1) return;
@@ -257,15 +271,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     for (int dc = 0; dc < NDC; ++dc)
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(Qs, 0, dc, lane), kb[dc], s, 0,
                                                   0, 0);
-    // Pairs outside the band (or past n) get a -inf score, so P = 0 there.
-    // One wave-uniform branch, kept apart from the straight-line code below
-    // so that the compiler can interleave its MFMAs with vector work.
+    // -lse in base 2 per query row; pairs outside the band (or past n) get
+    // -inf instead, so that P = exp2(S*scale*log2e - lse*log2e) = 0 there.
+    // One wave-uniform branch of selects on these values (not on the MFMA
+    // results), kept apart from the straight-line code below so that the
+    // compiler can interleave its MFMAs with vector work.
+    float nl[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) nl[r] = -l4[r >> 2][r & 3] * log2e;
     if (!full) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qi = q0 + 8 * (r >> 2) + 4 * hi + (r & 3);
         const bool vis = qi < n && key < n && key >= lo_of(qi) && key <= hi_of(qi);
-        if (!vis) s[r] = kNegInf;
+        nl[r] = vis ? nl[r] : kNegInf;
       }
     }
     // dP = dO V^T on the matrix cores while the vector unit forms P.
@@ -277,7 +296,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     bf16x8 pbf[2], dsbf[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      p[r] = exp2_fast(__builtin_fmaf(s[r], c2, -l4[r >> 2][r & 3] * log2e));
+      p[r] = exp2_fast(__builtin_fmaf(s[r], c2, nl[r]));
       pbf[r >> 3][r & 7] = (__bf16)p[r];
     }
     // dV += P^T dO while the vector unit forms dS.  MFMA k index 8*hi + t of
@@ -301,20 +320,56 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
             dsbf[c], tr_frag<D>(Qs, 16 * c, 32 * db, lane), dk[db], 0, 0, 0);
   };
 
-  stage(0, sQ0, sO0, sL0, sD0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  for (int t = 0; t < T; t += 2) {
-    if (t + 1 < T) stage(t + 1, sQ1, sO1, sL1, sD1);
-    tile(t, sQ0, sO0, sL0, sD0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+  // Three buffers: the tiles two steps ahead are in flight while a tile is
+  // used.  A stage is 2*IPW + 1 loads per wave and loads complete in issue
+  // order, so waiting until that many remain leaves exactly the newest stage
+  // in flight.  The barrier carries no memory fence (__syncthreads() would
+  // also wait for every load in flight): each wave has waited for its own
+  // part of the stage to use, and every LDS read of the buffer refilled next
+  // has returned its data before the wave reaches the barrier (the tile's
+  // products consumed it).  The empty asm statements keep the compiler from
+  // moving memory accesses across.
+  constexpr int kPerStage = 2 * IPW + 1;
+  static_assert(kPerStage < 16, "vmcnt immediate in its low field");
+  auto wait_newest = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0F70 | kPerStage);  // vmcnt(kPerStage)
+  };
+  auto barrier = [&]() __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  Cursor cs{0, qt_hi}, ct{0, qt_hi};
+  stage(0, cs, sB0);
+  advance(cs);
+  stage(1, cs, sB1);
+  advance(cs);
+  wait_newest();
+  barrier();
+  for (int t = 0;; t += 3) {
+    stage(t + 2, cs, sB2);
+    advance(cs);
+    tile(ct.qt, sB0);
+    advance(ct);
+    wait_newest();
+    barrier();
     if (t + 1 >= T) break;
-    if (t + 2 < T) stage(t + 2, sQ0, sO0, sL0, sD0);
-    tile(t + 1, sQ1, sO1, sL1, sD1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    stage(t + 3, cs, sB0);
+    advance(cs);
+    tile(ct.qt, sB1);
+    advance(ct);
+    wait_newest();
+    barrier();
+    if (t + 2 >= T) break;
+    stage(t + 4, cs, sB1);
+    advance(cs);
+    tile(ct.qt, sB2);
+    advance(ct);
+    wait_newest();
+    barrier();
+    if (t + 3 >= T) break;
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   if (!wave_keys) return;
   // dK = scale * acc; lane holds dims 32*db + l32 of keys kw0 + rho(r).
