@@ -265,20 +265,35 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       l4[j] = *reinterpret_cast<const f32x4*>(Ls + 8 * j + 4 * hi);
       d4[j] = *reinterpret_cast<const f32x4*>(Ds + 8 * j + 4 * hi);
     }
-    // S = Q K^T: lane owns key kw0 + l32 and query rows rho(r).
+    // The tile is one stream of 4*NDC products, each with one operand
+    // fragment read from LDS two products ahead: S = Q K^T (Q rows; lane: key
+    // l32, 16 query rows), dP = dO V^T (dO rows), dV += P^T dO (dO
+    // transposed), dK += dS^T Q (Q transposed).  The vector work rides
+    // between the products that do not depend on it: the base-2 -lse terms
+    // beside S, P beside dP, dS beside dV.  A scheduling fence after each
+    // product keeps this order.  In dV and dK the MFMA k index 8*hi + t of
+    // chunk c stands for query 16*c + 8*(t/4) + 4*hi + t%4, the order the
+    // accumulator holds.
     f32x16 s = f32x16{}, dp = f32x16{};
+    float nl[16], p[16];
+    bf16x8 pbf[2], dsbf[2];
+    bf16x8 f0 = row_frag<D>(Qs, 0, 0, lane);
+    bf16x8 f1 = row_frag<D>(Qs, 0, 1, lane);
+    constexpr int RPK = 16 / NDC;  // rows of vector work per product
 #pragma unroll
-    for (int dc = 0; dc < NDC; ++dc)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(Qs, 0, dc, lane), kb[dc], s, 0,
-                                                  0, 0);
-    // -lse in base 2 per query row; pairs outside the band (or past n) get
-    // -inf instead, so that P = exp2(S*scale*log2e - lse*log2e) = 0 there.
-    // One wave-uniform branch of selects on these values (not on the MFMA
-    // results), kept apart from the straight-line code below so that the
-    // compiler can interleave its MFMAs with vector work.
-    float nl[16];
+    for (int dc = 0; dc < NDC; ++dc) {
+      const bf16x8 f2 = dc + 2 < NDC ? row_frag<D>(Qs, 0, dc + 2, lane)
+                                     : row_frag<D>(Os, 0, dc + 2 - NDC, lane);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0, kb[dc], s, 0, 0, 0);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) nl[r] = -l4[r >> 2][r & 3] * log2e;
+      for (int r = RPK * dc; r < RPK * (dc + 1); ++r) nl[r] = -l4[r >> 2][r & 3] * log2e;
+      f0 = f1;
+      f1 = f2;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // -inf for pairs outside the band (or past n): P = 0 there.  A
+    // wave-uniform branch of selects on the -lse terms, not on the MFMA
+    // results.
     if (!full) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -287,37 +302,51 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         nl[r] = vis ? nl[r] : kNegInf;
       }
     }
-    // dP = dO V^T on the matrix cores while the vector unit forms P.
 #pragma unroll
-    for (int dc = 0; dc < NDC; ++dc)
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(Os, 0, dc, lane), vb[dc], dp, 0,
-                                                   0, 0);
-    float p[16];
-    bf16x8 pbf[2], dsbf[2];
+    for (int dc = 0; dc < NDC; ++dc) {
+      const bf16x8 f2 = dc + 2 < NDC ? row_frag<D>(Os, 0, dc + 2, lane)
+                                     : tr_frag<D>(Os, 0, 32 * (dc + 2 - NDC), lane);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0, vb[dc], dp, 0, 0, 0);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      p[r] = exp2_fast(__builtin_fmaf(s[r], c2, nl[r]));
-      pbf[r >> 3][r & 7] = (__bf16)p[r];
+      for (int r = RPK * dc; r < RPK * (dc + 1); ++r) {
+        p[r] = exp2_fast(__builtin_fmaf(s[r], c2, nl[r]));
+        pbf[r >> 3][r & 7] = (__bf16)p[r];
+      }
+      f0 = f1;
+      f1 = f2;
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // dV += P^T dO while the vector unit forms dS.  MFMA k index 8*hi + t of
-    // chunk c stands for query 16*c + 8*(t/4) + 4*hi + t%4, the order the
-    // accumulator holds.
+    // dS rows formed beside dV product u: none beside the first (it would
+    // wait for dP to finish), the 16 spread over the rest.
+    constexpr int NU = 2 * NDB;  // products in dV (and in dK)
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int u = 0; u < NU; ++u) {
+      const int c = u / NDB, db = u % NDB;
+      const int un = u + 2;
+      const bf16x8 f2 = un < NU ? tr_frag<D>(Os, 16 * (un / NDB), 32 * (un % NDB), lane)
+                                : tr_frag<D>(Qs, 16 * ((un - NU) / NDB), 32 * ((un - NU) % NDB), lane);
+      dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pbf[c], f0, dv[db], 0, 0, 0);
+      const int r0 = u == 0 ? 0 : ((u - 1) * 16 + NU - 2) / (NU - 1);
+      const int r1 = ((u) * 16 + NU - 2) / (NU - 1);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            pbf[c], tr_frag<D>(Os, 16 * c, 32 * db, lane), dv[db], 0, 0, 0);
+      for (int r = 0; r < 16; ++r)
+        if (u > 0 && r >= r0 && r < r1)
+          dsbf[r >> 3][r & 7] = (__bf16)(p[r] * (dp[r] - d4[r >> 2][r & 3]));
+      f0 = f1;
+      f1 = f2;
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      dsbf[r >> 3][r & 7] = (__bf16)(p[r] * (dp[r] - d4[r >> 2][r & 3]));
-    // dK += dS^T Q.
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            dsbf[c], tr_frag<D>(Qs, 16 * c, 32 * db, lane), dk[db], 0, 0, 0);
+    for (int u = 0; u < NU; ++u) {
+      const int c = u / NDB, db = u % NDB;
+      const int un = u + 2;
+      bf16x8 f2 = f1;
+      if (un < NU) f2 = tr_frag<D>(Qs, 16 * (un / NDB), 32 * (un % NDB), lane);
+      dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsbf[c], f0, dk[db], 0, 0, 0);
+      f0 = f1;
+      f1 = f2;
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   // Three buffers: the tiles two steps ahead are in flight while a tile is
