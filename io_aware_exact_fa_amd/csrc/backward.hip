@@ -15,7 +15,7 @@
 //   * bwd_dkdv_kernel: a workgroup owns 128 keys of one (b, KV head); wave w
 //     owns 32 of them with K and V held in registers as MFMA B operands.  It
 //     streams (32-query tile, query head) pairs, top tile first, through
-//     double-buffered LDS:
+//     three LDS stage buffers (each tile's loads issued two tiles ahead):
 //     S = Q K^T and dP = dO V^T (v_mfma_f32_32x32x16_bf16; in the accumulator
 //     lane l owns key l%32 and 16 query rows), P and dS elementwise, then
 //     dV += P^T dO and dK += dS^T Q with P^T / dS^T taken straight from those
