@@ -104,10 +104,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, 0x00020000);
 }
 
+// Every K/V byte of the cache is read once per launch: the page loads carry
+// the non-temporal hint (cache-policy bit nt), which let a plain 16-byte-per-
+// lane stream over 4 GiB read at 6.94 TB/s instead of 6.25.
+constexpr int kStream = 2;
+
 // 16 bytes per lane from HBM straight into LDS (lane i -> lds + 16*i).
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, unsigned off, void* lds) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
-                                           off, 0, 0, 0);
+                                           off, 0, 0, kStream);
 }
 
 // Eight E4M3 bytes (little-endian in two words) widened to bf16; exact, as
@@ -237,11 +242,11 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
 #pragma unroll
       for (int m = 0; m < NC / 2; ++m)
         r.k[m] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, col * D + 64 * m + 16 * grp, 0, 0));
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, col * D + 64 * m + 16 * grp, 0, kStream));
 #pragma unroll
       for (int j = 0; j < D / 64; ++j)
         r.v[j] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, 1024 * j + 16 * lane, 0, 0));
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, 1024 * j + 16 * lane, 0, kStream));
     } else {
       const int nb = i < cnt ? PAGE_BYTES : 0;
       const __amdgpu_buffer_rsrc_t rk = page_rsrc(a.kc + base, nb);
@@ -250,7 +255,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
 #pragma unroll
       for (int j = 0; j < NC; ++j)
         r.k[j] = __builtin_bit_cast(
-            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, 1024 * j + 16 * lane, 0, 0));
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, 1024 * j + 16 * lane, 0, kStream));
 #pragma unroll
       for (int j = 0; j < NVJ; ++j) dma16(rv, v_off[j], vdst + 1024 * j);
     }
