@@ -496,23 +496,22 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 }
 
 // Pages per split.  Long splits amortise each workgroup's start-up (lengths,
-// page ids, first page) and its end (merge of the 4 waves); measured on the
-// 64-sequence workload, 80-120 pages is best.  With few sequences x heads the
-// split shrinks so that enough workgroups exist: the estimate uses H/4 KV
-// heads and half of max_seqlen as the typical length.  Exact powers of two
-// from 64 up are avoided: with the split index fastest in the grid they
-// measured ~15 % slower.
+// page ids, first page) and its end (merge of the 4 waves); on the
+// 64-sequence workload (up to 2048 pages) 120 pages measured best among 72
+// to 240 (0.675 ms against 0.682 at 96 and 0.709 at 72).  With few
+// sequences x heads the split shrinks so that enough workgroups exist: the
+// estimate uses H/4 KV heads and half of max_seqlen as the typical length.
 int decode_split_pages(int B, int H, int max_seqlen) {
   const long long max_pages = ((long long)max_seqlen + kPage - 1) / kPage;
   const long long groups = (long long)B * (H >= 4 ? H / 4 : 1);
   const long long avg_pages = (max_pages + 1) / 2;
-  int sp = 96;
-  while (sp > 8 && groups * ((avg_pages + sp - 1) / sp) < 2048) sp = sp > 12 ? sp / 2 : 8;
+  int sp = 120;
+  while (sp > 8 && groups * ((avg_pages + sp - 1) / sp) < 2048) sp = sp > 16 ? sp / 2 : 8;
   return sp;
 }
 // A wave holds the page ids of its share of a split one per lane and reads
 // lane cnt (one past its last page) for the final prefetch.
-static_assert((96 + kDecodeWaves - 1) / kDecodeWaves + 1 <= 64,
+static_assert((120 + kDecodeWaves - 1) / kDecodeWaves + 1 <= 64,
               "a wave's pages plus one must fit in 64 lanes");
 
 int decode_max_splits(int B, int H, int max_seqlen) {
@@ -529,9 +528,21 @@ size_t decode_workspace_bytes(int B, int H, int max_seqlen, int d) {
   return align_up(rows * d * sizeof(float), 256) + align_up(rows * sizeof(float), 256);
 }
 
+// The split index is fastest in the grid and workgroups go round-robin over
+// the 8 XCDs in dispatch order, so with a split count that is a multiple of 8
+// split s of every (KV head, sequence) row lands on XCD s mod 8: the low
+// splits, live in every sequence, crowd a few XCDs while the high ones sit
+// idle (16 splits of 136 pages: 0.84 ms, against 0.69 with 17).  One more
+// split per row, empty (it starts past every sequence's last page and exits
+// at once), rotates the rows over the XCDs.
+static int decode_grid_splits(int max_splits) {
+  return max_splits % 8 == 0 ? max_splits + 1 : max_splits;
+}
+
 template <int D, int GP, bool FP8>
 static void launch_split(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<D, GP, FP8>), dim3(a.max_splits, a.Hkv, a.B),
+  hipLaunchKernelGGL((decode_split_kernel<D, GP, FP8>),
+                     dim3(decode_grid_splits(a.max_splits), a.Hkv, a.B),
                      dim3(kDecodeWaves * 64), 0, stream, a);
 }
 

@@ -81,3 +81,22 @@ def test_decode_full_size_all_outputs(d):
     o, lse = _run(meta, 32768)
     o_ref, lse_ref = decode_oracle_all(meta, 1.0 / math.sqrt(d))
     compare(o, lse, o_ref, lse_ref, TOL_BF16, f"decode full size d{d} (all 64 sequences)")
+
+
+def test_decode_split_count_multiple_of_8():
+    """16 sequences up to 30000 tokens: 60-page splits, 32 of them per
+    (sequence, KV head) row, so the launch adds one empty split per row (a
+    split count that is a multiple of 8 is padded).  The longest sequence
+    fills the last real split; every output against the oracle."""
+    import io_aware_exact_fa_amd as fa
+    lens = [30000, 1024, 29999, 960, 15000, 7681, 23040, 28801, 3000, 1, 12345, 29000,
+            17, 26000, 4097, 19200]
+    max_len = 30000
+    assert fa.fa_decode_workspace_bytes(16, 32, max_len, 128) == \
+        16 * 32 * 32 * (128 + 1) * 4   # 32 splits of 60 pages per row
+    say(f"case decode B16 H32 Hkv8 d128 max_len {max_len} (32 splits, padded grid)")
+    meta = decode_inputs(16, 32, 8, 128, 16, 1, max_len, seed=71, seqlens=lens,
+                         with_values=False)
+    o, lse = _run(meta, max_len)
+    o_ref, lse_ref = decode_oracle_all(meta, 1.0 / math.sqrt(128))
+    compare(o, lse, o_ref, lse_ref, TOL_BF16, "decode B16 padded split grid")
