@@ -217,7 +217,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
   struct PageK {
     bf16x8 k[NC];
   };
-  struct PageK8 {  // FP8: the page's key and value bytes held by this lane
+  struct PageK8 {  // FP8: a page's key bytes (k) or value bytes (v) held by this lane
     u32x4 k[NC / 2];   // token col, dims 64m + 16*grp .. +15
     u32x4 v[D / 64];   // 16-byte piece 64j + lane of the page (row-major)
   };
@@ -226,28 +226,15 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
     int phys = __builtin_amdgcn_readlane(my_phys, i);
     return (phys < 0 || phys >= a.num_pages) ? -1 : phys;
   };
-  // Page i: K into registers (MFMA A layout: token lane%16, dims 32c +
-  // 8*(lane/16) .. +8) and V into the LDS buffer vdst by DMA.  An invalid page
-  // id loads page 0 (in bounds) and its tokens are masked; a page past the
+  // bf16 page i: K into registers (lane-linear 16-byte pieces, rearranged
+  // through LDS before use) and V into the LDS buffer vdst by DMA.  An invalid
+  // page id loads page 0 (in bounds) and its tokens are masked; a page past the
   // wave's last one (i >= cnt) loads nothing (zero-sized range).
   auto load_page = [&](int i, PageRegs& r, char* vdst) {
     int phys = phys_of(i);
     if (phys < 0) phys = 0;
     const size_t base = ((size_t)phys * a.Hkv + g) * kPage * D;
-    if constexpr (FP8) {
-      (void)vdst;
-      const int nb = i < cnt ? kPage * D : 0;
-      const __amdgpu_buffer_rsrc_t rk = page_rsrc(a.kc8 + base, nb);
-      const __amdgpu_buffer_rsrc_t rv = page_rsrc(a.vc8 + base, nb);
-#pragma unroll
-      for (int m = 0; m < NC / 2; ++m)
-        r.k[m] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, col * D + 64 * m + 16 * grp, 0, kStream));
-#pragma unroll
-      for (int j = 0; j < D / 64; ++j)
-        r.v[j] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, 1024 * j + 16 * lane, 0, kStream));
-    } else {
+    if constexpr (!FP8) {
       const int nb = i < cnt ? PAGE_BYTES : 0;
       const __amdgpu_buffer_rsrc_t rk = page_rsrc(a.kc + base, nb);
       const __amdgpu_buffer_rsrc_t rv = page_rsrc(a.vc + base, nb);
@@ -260,8 +247,33 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
       for (int j = 0; j < NVJ; ++j) dma16(rv, v_off[j], vdst + 1024 * j);
     }
   };
+  // FP8 page i, into registers: its key bytes (keys = true; token col, dims
+  // 64m + 16*grp .. +15) or its value bytes (16-byte piece 64j + lane of the
+  // row-major slab).  Same page-id and range rules as above.
+  auto load_page8 = [&](int i, PageRegs& r, bool keys) {
+    int phys = phys_of(i);
+    if (phys < 0) phys = 0;
+    const size_t base = ((size_t)phys * a.Hkv + g) * kPage * D;
+    const int nb = i < cnt ? kPage * D : 0;
+    if constexpr (FP8) {
+      if (keys) {
+        const __amdgpu_buffer_rsrc_t rk = page_rsrc(a.kc8 + base, nb);
+#pragma unroll
+        for (int m = 0; m < NC / 2; ++m)
+          r.k[m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rk, col * D + 64 * m + 16 * grp, 0, kStream));
+      } else {
+        const __amdgpu_buffer_rsrc_t rv = page_rsrc(a.vc8 + base, nb);
+#pragma unroll
+        for (int j = 0; j < D / 64; ++j)
+          r.v[j] = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, 1024 * j + 16 * lane, 0, kStream));
+      }
+    }
+  };
 
-  auto process_page = [&](int i, const PageRegs& r, const char* vsrc) {
+  // Page i with its keys in rk (both paths) and, FP8, its values in rv.
+  auto process_page = [&](int i, const PageRegs& r, const PageRegs& rvv, const char* vsrc) {
     const bool valid = phys_of(i) >= 0;
     const int tok0 = (p0 + wave + kDecodeWaves * i) * kPage;
     const int lim = valid ? L : tok0;  // tokens at or past lim are masked
@@ -278,8 +290,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
       for (int j = 0; j < D / 64; ++j) {
         const int piece = 64 * j + lane, r8 = piece / (D / 16), k8 = piece % (D / 16);
         char* dst = const_cast<char*>(vsrc) + r8 * D * 2 + 16 * ((2 * k8) ^ vswz<D>(r8));
-        *reinterpret_cast<bf16x8*>(dst) = e4m3x8_to_bf16(u32x2{r.v[j][0], r.v[j][1]});
-        *reinterpret_cast<bf16x8*>(dst + 16) = e4m3x8_to_bf16(u32x2{r.v[j][2], r.v[j][3]});
+        *reinterpret_cast<bf16x8*>(dst) = e4m3x8_to_bf16(u32x2{rvv.v[j][0], rvv.v[j][1]});
+        *reinterpret_cast<bf16x8*>(dst + 16) = e4m3x8_to_bf16(u32x2{rvv.v[j][2], rvv.v[j][3]});
       }
 #pragma unroll
       for (int m = 0; m < NC / 2; ++m) {
@@ -359,17 +371,45 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_split_kernel(DecodeA
     }
   };
 
-  // Two page register sets and two V buffers: page i+1 is in flight while
-  // page i is processed.  (For FP8 a second page in flight costs the
-  // registers of a third wave per SIMD and measured slower.)
-  PageRegs ka, kb;
-  load_page(0, ka, sV0[wave]);
-  for (int i = 0; i < cnt; i += 2) {
-    load_page(i + 1, kb, sV1[wave]);
-    process_page(i, ka, sV0[wave]);
-    if (i + 1 >= cnt) break;
-    load_page(i + 2, ka, sV0[wave]);
-    process_page(i + 1, kb, sV1[wave]);
+  // bf16: two page register sets and two V buffers, page i+1 in flight while
+  // page i is processed.  FP8: keys two pages ahead (three register sets),
+  // values one (two sets), which still fits three waves per SIMD (whole FP8
+  // pages two ahead would not); the loop is unrolled by six so that every
+  // set is a fixed register range.
+  if constexpr (FP8) {
+    PageRegs k0, k1, k2, v0, v1;
+    load_page8(0, k0, true);
+    load_page8(0, v0, false);
+    load_page8(1, k1, true);
+    auto step = [&](int i, const PageRegs& kc, const PageRegs& vc, PageRegs& kn, PageRegs& vn,
+                    const char* vsrc) __attribute__((always_inline)) {
+      load_page8(i + 2, kn, true);
+      load_page8(i + 1, vn, false);
+      process_page(i, kc, vc, vsrc);
+    };
+    for (int i = 0; i < cnt; i += 6) {
+      step(i, k0, v0, k2, v1, sV0[wave]);
+      if (i + 1 >= cnt) break;
+      step(i + 1, k1, v1, k0, v0, sV1[wave]);
+      if (i + 2 >= cnt) break;
+      step(i + 2, k2, v0, k1, v1, sV0[wave]);
+      if (i + 3 >= cnt) break;
+      step(i + 3, k0, v1, k2, v0, sV1[wave]);
+      if (i + 4 >= cnt) break;
+      step(i + 4, k1, v0, k0, v1, sV0[wave]);
+      if (i + 5 >= cnt) break;
+      step(i + 5, k2, v1, k1, v0, sV1[wave]);
+    }
+  } else {
+    PageRegs ka, kb;
+    load_page(0, ka, sV0[wave]);
+    for (int i = 0; i < cnt; i += 2) {
+      load_page(i + 1, kb, sV1[wave]);
+      process_page(i, ka, ka, sV0[wave]);
+      if (i + 1 >= cnt) break;
+      load_page(i + 2, ka, sV0[wave]);
+      process_page(i + 1, kb, kb, sV1[wave]);
+    }
   }
 
   // The last prefetch (past the wave's pages, zero-sized) may still be in
