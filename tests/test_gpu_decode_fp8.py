@@ -110,3 +110,17 @@ def test_decode_fp8_zero_and_negative_key_scale(ks):
         # uniform softmax over L keys: lse = ln L for the two query heads of KV head 1
         want = np.repeat(np.log(np.array(lens, dtype=np.float64))[:, None], 2, axis=1)
         np.testing.assert_allclose(lse[:, 2:4], want, rtol=0, atol=1e-5)
+
+
+def test_decode_fp8_split_count_multiple_of_8():
+    """The padded split grid with an E4M3 cache: 16 sequences up to 30000
+    tokens, 32 splits of 60 pages per row (launched as 33), 15 pages per wave
+    (every position of the six-page key/value rotation); every output."""
+    lens = [30000, 1024, 29999, 960, 15000, 7681, 23040, 28801, 3000, 1, 12345, 29000,
+            17, 26000, 4097, 19200]
+    say("decode fp8 B16 H32 Hkv8 d128 max_len 30000 (32 splits, padded grid)")
+    meta = decode_fp8_inputs(16, 32, 8, 128, 16, 1, 30000, seed=72, seqlens=lens)
+    scale = 1.0 / math.sqrt(128)
+    o, lse = run_fp8(meta, 8, scale)
+    o_ref, lse_ref = decode_oracle_all(meta, scale, fp8=True)
+    compare(o, lse, o_ref, lse_ref, TOL_BF16, "decode fp8 B16 padded split grid")
