@@ -550,9 +550,9 @@ int decode_split_pages(int B, int H, int max_seqlen) {
   return sp;
 }
 // A wave holds the page ids of its share of a split one per lane and reads
-// lane cnt (one past its last page) for the final prefetch.
-static_assert((120 + kDecodeWaves - 1) / kDecodeWaves + 1 <= 64,
-              "a wave's pages plus one must fit in 64 lanes");
+// up to lane cnt + 1 (the FP8 keys are prefetched two pages ahead).
+static_assert((120 + kDecodeWaves - 1) / kDecodeWaves + 2 <= 64,
+              "a wave's pages plus two must fit in 64 lanes");
 
 int decode_max_splits(int B, int H, int max_seqlen) {
   const int sp = decode_split_pages(B, H, max_seqlen);
