@@ -154,6 +154,38 @@ def test_workspace_size(lib):
     assert _dec(wsb=ws - 1) == -4
 
 
+def _decode_plan_bytes(B, H, max_seqlen, d):
+    """The documented split plan: 120 pages (1920 tokens) per split, halved
+    (down to 8) while fewer than 2048 (sequence, H/4 head group) splits of an
+    average sequence (half of max_seqlen) would exist; one partial (d floats)
+    and one log-sum-exp per (sequence, query head, split), each array padded
+    to 256 bytes.  Padding the launch grid by an empty split adds no partial."""
+    pages = -(-max_seqlen // 16)
+    groups = B * (H // 4 if H >= 4 else 1)
+    avg = (pages + 1) // 2
+    sp = 120
+    while sp > 8 and groups * (-(-avg // sp)) < 2048:
+        sp = sp // 2 if sp > 16 else 8
+    rows = B * H * (-(-pages // sp))
+    up = lambda x: -(-x // 256) * 256
+    return up(rows * d * 4) + up(rows * 4)
+
+
+@pytest.mark.parametrize("B,H,max_seqlen,d", [
+    (64, 32, 32768, 128), (64, 32, 32768, 64), (16, 32, 30000, 128), (5, 32, 4136, 128),
+    (1, 8, 1, 128), (2, 16, 1500, 64), (128, 32, 65536, 128), (3, 2, 777, 128),
+    (64, 32, 30000, 128), (8, 64, 131072, 128),
+])
+def test_decode_workspace_follows_split_plan(lib, B, H, max_seqlen, d):
+    assert fa.fa_decode_workspace_bytes(B, H, max_seqlen, d) == _decode_plan_bytes(B, H, max_seqlen, d)
+
+
+def test_decode_split_plan_of_the_workload(lib):
+    """The 64-sequence workload (up to 32768 tokens): 18 splits of 120 pages."""
+    rows = 64 * 32 * 18
+    assert fa.fa_decode_workspace_bytes(64, 32, 32768, 128) == rows * 128 * 4 + rows * 4
+
+
 def _bwd(**kw):
     args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
                 B=1, H=2, Hkv=1, n=16, d=128, causal=0, window=-1, scale=0.1, dtype=0,
